@@ -1,0 +1,383 @@
+// C ABI of the MoE layer library: argument validation, workspace carving and
+// launch sequencing.  Every check runs before the first enqueue, so a
+// rejected call writes nothing and makes no GPU call.
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elt_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+bool is_pk(const moe_dims* d) { return d->router_kind == MOE_ROUTER_PRODUCT_KEY; }
+
+int32_t validate_dims(const moe_dims* d, int64_t T) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (d->d <= 0 || d->d % 64 != 0 || d->d > 8192) return MOE_ERR_SHAPE;
+  if (d->k < 1 || d->k > MOE_MAX_K || d->k > d->E) return MOE_ERR_SHAPE;
+  if (T * (int64_t)d->k > INT32_MAX) return MOE_ERR_SHAPE;
+  if (T * (int64_t)d->d > ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  if (!(d->ffn_logit_scale == d->ffn_logit_scale) || isinf(d->ffn_logit_scale))
+    return MOE_ERR_SHAPE;
+  if (d->n_shared < 0 || d->n_shared > 64) return MOE_ERR_SHAPE;
+  if (d->n_shared > 0 && (d->f_shared <= 0 || d->f_shared % 64 != 0)) return MOE_ERR_SHAPE;
+  if (d->router_kind == MOE_ROUTER_SOFTMAX_TOPK) {
+    if (d->E < 1 || d->E > MOE_MAX_E_SOFTMAX) return MOE_ERR_SHAPE;
+    if (d->E_ffn < 0 || d->E_ffn > d->E || d->E - d->E_ffn > MOE_MAX_ZC) return MOE_ERR_SHAPE;
+    for (int z = 0; z < d->E - d->E_ffn; z++)
+      if (d->zc_kind[z] < MOE_ZC_ZERO || d->zc_kind[z] > MOE_ZC_CONST) return MOE_ERR_SHAPE;
+    if (d->E_ffn > 0 && (d->f <= 0 || d->f % 64 != 0)) return MOE_ERR_SHAPE;
+  } else if (d->router_kind == MOE_ROUTER_PRODUCT_KEY) {
+    if (d->E_ffn != 0) return MOE_ERR_SHAPE;
+    if (d->pk_rows < 1 || d->pk_cols < 1 || d->pk_rows > MOE_MAX_PK_SIDE ||
+        d->pk_cols > MOE_MAX_PK_SIDE)
+      return MOE_ERR_SHAPE;
+    if ((int64_t)d->pk_rows * d->pk_cols != d->E) return MOE_ERR_SHAPE;
+    if (d->pk_k_row < 1 || d->pk_k_row > d->pk_rows || d->pk_k_row > 64) return MOE_ERR_SHAPE;
+    if (d->pk_k_col < 1 || d->pk_k_col > d->pk_cols || d->pk_k_col > 64) return MOE_ERR_SHAPE;
+    if ((int64_t)d->pk_k_row * d->pk_k_col > MOE_MAX_PK_CAND) return MOE_ERR_SHAPE;
+    if (d->k > d->pk_k_row * d->pk_k_col) return MOE_ERR_SHAPE;
+  } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int n_const_of(const moe_dims* d) {
+  int c = 0;
+  if (d->router_kind != MOE_ROUTER_SOFTMAX_TOPK) return 0;
+  for (int z = 0; z < d->E - d->E_ffn; z++) c += d->zc_kind[z] == MOE_ZC_CONST;
+  return c;
+}
+
+bool misaligned(const void* p) { return p && ((uintptr_t)p % 16) != 0; }
+
+// Workspace layout (one figure for every entry point).
+struct Layout {
+  int64_t T, n;
+  int NL, Kw, BM;
+  int64_t max_tiles;
+  size_t w3, logits, disp, tiles, ntiles, h, hs, idx, gate, counts, offsets, perm, inv, y, sy;
+  size_t total;
+};
+
+Layout make_layout(const moe_dims* d, int64_t T) {
+  Layout L;
+  L.T = T;
+  L.n = T * d->k;
+  const int es = elt_size(d->dtype);
+  if (is_pk(d)) {
+    L.NL = d->pk_rows + d->pk_cols;
+    L.Kw = d->d / 2;
+  } else {
+    L.NL = d->E;
+    L.Kw = d->d;
+  }
+  L.BM = gemm_tile_rows(d->dtype, L.n, d->E_ffn);
+  const int E_groups = is_pk(d) ? 0 : d->E_ffn;
+  L.max_tiles = gemm_max_tiles(T, is_pk(d) ? 0 : d->k, E_groups, d->n_shared, L.BM);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L.w3 = take(d->dtype == MOE_BF16 ? (size_t)3 * L.NL * L.Kw * 2 : 0);
+  L.logits = take((size_t)T * L.NL * 4);
+  L.disp = take((size_t)dispatch_scratch_ints(L.n, d->E) * 4);
+  L.tiles = take((size_t)L.max_tiles * sizeof(int4));
+  L.ntiles = take(4);
+  L.h = take(is_pk(d) ? 0 : (size_t)L.n * d->f * es);
+  L.hs = take((size_t)d->n_shared * T * d->f_shared * es);
+  L.idx = take((size_t)L.n * 4);
+  L.gate = take((size_t)L.n * 4);
+  L.counts = take((size_t)d->E * 4);
+  L.offsets = take((size_t)(d->E + 1) * 4);
+  L.perm = take((size_t)L.n * 4);
+  L.inv = take((size_t)L.n * 4);
+  L.y = take(is_pk(d) ? (size_t)L.n * 4 : (size_t)L.n * d->d * es);
+  L.sy = take((size_t)d->n_shared * T * d->d * es);
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P at(void* ws, size_t off) {
+  return reinterpret_cast<P>(reinterpret_cast<char*>(ws) + off);
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                          \
+  do {                                         \
+    int32_t _s = hip_status(expr);             \
+    if (_s != MOE_OK) return _s;               \
+  } while (0)
+
+int32_t check_weights(const moe_dims* d, const moe_weights* w, bool router, bool experts,
+                      bool combine) {
+  if (!w) return MOE_ERR_NULL;
+  if (router && !w->router_w) return MOE_ERR_NULL;
+  if (experts && !is_pk(d) && d->E_ffn > 0 && (!w->w_gate || !w->w_up || !w->w_down))
+    return MOE_ERR_NULL;
+  if (experts && d->n_shared > 0 && (!w->shared_gate || !w->shared_up || !w->shared_down))
+    return MOE_ERR_NULL;
+  if (experts && is_pk(d) && !w->atom_u) return MOE_ERR_NULL;
+  if (combine && is_pk(d) && !w->atom_w) return MOE_ERR_NULL;
+  if (combine && n_const_of(d) > 0 && (!w->const_wc || !w->const_v)) return MOE_ERR_NULL;
+  const void* ps[] = {w->router_w, w->router_bias, w->w_gate, w->w_up, w->w_down,
+                      w->shared_gate, w->shared_up, w->shared_down, w->const_wc, w->const_v,
+                      w->atom_u, w->atom_w};
+  for (const void* p : ps)
+    if (misaligned(p)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- stages
+
+int32_t do_route(const moe_dims* d, const moe_weights* w, const void* x, int64_t T, int32_t* idx,
+                 float* gate, void* ws, const Layout& L, hipStream_t st) {
+  float* logits = at<float*>(ws, L.logits);
+  const void* W = w->router_w;
+  if (d->dtype == MOE_BF16) {
+    uint16_t* w3 = at<uint16_t*>(ws, L.w3);
+    MOE_TRY(launch_split_router(w->router_w, w3, (int64_t)L.NL * L.Kw, st));
+    W = w3;
+  }
+  const int64_t slice = (int64_t)L.NL * L.Kw;
+  const int es = elt_size(d->dtype);
+  if (!is_pk(d)) {
+    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, slice, d->E, d->d, logits, d->E, 0,
+                                 st));
+    MOE_TRY(launch_select_topk(logits, T, d->E, d->E_ffn, d->k, d->ffn_logit_scale,
+                               w->router_bias, d->renorm, idx, gate, st));
+  } else {
+    const int K = L.Kw;
+    const void* Wc = reinterpret_cast<const char*>(W) + (size_t)d->pk_rows * K * (d->dtype == MOE_BF16 ? 2 : 4);
+    (void)es;
+    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, slice, d->pk_rows, K, logits, L.NL,
+                                 0, st));
+    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, K, Wc, slice, d->pk_cols, K, logits, L.NL,
+                                 d->pk_rows, st));
+    MOE_TRY(launch_select_pk(logits, T, d->pk_rows, d->pk_cols, d->pk_k_row, d->pk_k_col, d->k,
+                             idx, gate, st));
+  }
+  return MOE_OK;
+}
+
+int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64_t T,
+                   const int32_t* idx, const int32_t* perm, const int32_t* offsets, void* y,
+                   void* shared_y, void* ws, const Layout& L, hipStream_t st) {
+  if (is_pk(d)) {
+    MOE_TRY(launch_atomic_h(d->dtype, x, w->atom_u, idx, perm, L.n, d->k, d->d, (float*)y, st));
+  }
+  const int E_groups = is_pk(d) ? 0 : d->E_ffn;
+  if (E_groups == 0 && d->n_shared == 0) return MOE_OK;
+  int4* tiles = at<int4*>(ws, L.tiles);
+  int32_t* ntiles = at<int32_t*>(ws, L.ntiles);
+  MOE_TRY(launch_build_tiles(offsets, E_groups, d->n_shared, T, L.BM, tiles, ntiles, st));
+  void* H = at<void*>(ws, L.h);
+  void* Hs = at<void*>(ws, L.hs);
+  GemmArgs g1;
+  memset(&g1, 0, sizeof(g1));
+  g1.tiles = tiles;
+  g1.ntiles = ntiles;
+  g1.E_ffn = E_groups;
+  g1.T = T;
+  g1.a_x = x;
+  g1.perm = perm;
+  g1.k = d->k;
+  g1.b0_routed = w->w_gate;
+  g1.b1_routed = w->w_up;
+  g1.b0_shared = w->shared_gate;
+  g1.b1_shared = w->shared_up;
+  g1.c_routed = H;
+  g1.c_shared = Hs;
+  g1.N_routed = E_groups ? d->f : 0;
+  g1.N_shared = d->n_shared ? d->f_shared : 0;
+  g1.K_routed = d->d;
+  g1.K_shared = d->d;
+  MOE_TRY(launch_grouped_gemm(d->dtype, true, L.BM, g1, L.max_tiles, st));
+  GemmArgs g2 = g1;
+  g2.a_x = nullptr;
+  g2.perm = nullptr;
+  g2.a_routed = H;
+  g2.a_shared = Hs;
+  g2.b0_routed = w->w_down;
+  g2.b1_routed = nullptr;
+  g2.b0_shared = w->shared_down;
+  g2.b1_shared = nullptr;
+  g2.c_routed = is_pk(d) ? nullptr : y;
+  g2.c_shared = shared_y;
+  g2.N_routed = E_groups ? d->d : 0;
+  g2.N_shared = d->n_shared ? d->d : 0;
+  g2.K_routed = E_groups ? d->f : 0;
+  g2.K_shared = d->n_shared ? d->f_shared : 0;
+  MOE_TRY(launch_grouped_gemm(d->dtype, false, L.BM, g2, L.max_tiles, st));
+  return MOE_OK;
+}
+
+int32_t do_combine(const moe_dims* d, const moe_weights* w, const void* x, int64_t T,
+                   const int32_t* idx, const float* gate, const int32_t* inv, const void* y,
+                   const void* shared_y, void* out, hipStream_t st) {
+  if (is_pk(d)) {
+    MOE_TRY(launch_atomic_combine(d->dtype, w->atom_w, idx, gate, inv, (const float*)y, shared_y,
+                                  d->n_shared, T, d->k, d->d, out, st));
+    return MOE_OK;
+  }
+  CombineArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.idx = idx;
+  a.gate = gate;
+  a.inv_perm = inv;
+  a.y = y;
+  a.shared_y = shared_y;
+  a.out = out;
+  a.const_wc = w->const_wc;
+  a.const_v = w->const_v;
+  a.T = T;
+  a.d = d->d;
+  a.k = d->k;
+  a.E_ffn = d->E_ffn;
+  a.n_shared = d->n_shared;
+  int ci = 0;
+  for (int z = 0; z < d->E - d->E_ffn; z++) {
+    a.zc_kind[z] = d->zc_kind[z];
+    a.const_index[z] = d->zc_kind[z] == MOE_ZC_CONST ? ci++ : -1;
+  }
+  MOE_TRY(launch_combine(d->dtype, a, st));
+  return MOE_OK;
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+
+extern "C" {
+
+const char* moe_status_str(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "bad shape, limit or alignment";
+    case MOE_ERR_DTYPE: return "unsupported dtype";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "unsupported request";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_workspace_size(const moe_dims* dims, int64_t T, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  int32_t s = validate_dims(dims, T);
+  if (s != MOE_OK) return s;
+  *bytes = make_layout(dims, T).total;
+  return MOE_OK;
+}
+
+static int32_t check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (L.total > 0 && !ws) return MOE_ERR_NULL;
+  if (misaligned(ws) || ((uintptr_t)ws % kAlign) != 0) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int32_t moe_route(const moe_dims* dims, const moe_weights* w, const void* x, int64_t T,
+                  int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                  moe_stream stream) {
+  int32_t s = validate_dims(dims, T);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(dims, w, true, false, false)) != MOE_OK) return s;
+  if (T > 0 && (!x || !topk_idx || !topk_gate)) return MOE_ERR_NULL;
+  if (misaligned(x)) return MOE_ERR_SHAPE;
+  Layout L = make_layout(dims, T);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  return do_route(dims, w, x, T, topk_idx, topk_gate, ws, L, (hipStream_t)stream);
+}
+
+int32_t moe_dispatch(const moe_dims* dims, const int32_t* topk_idx, int64_t T, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                     size_t ws_bytes, moe_stream stream) {
+  int32_t s = validate_dims(dims, T);
+  if (s != MOE_OK) return s;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_idx || !perm || !inv_perm)) return MOE_ERR_NULL;
+  Layout L = make_layout(dims, T);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  MOE_TRY(launch_dispatch(topk_idx, L.n, dims->E, counts, offsets, perm, inv_perm,
+                          at<int32_t*>(ws, L.disp), (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int32_t moe_expert_ffn(const moe_dims* dims, const moe_weights* w, const void* x, int64_t T,
+                       const int32_t* topk_idx, const int32_t* perm, const int32_t* offsets,
+                       void* y, void* shared_y, void* ws, size_t ws_bytes, moe_stream stream) {
+  int32_t s = validate_dims(dims, T);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(dims, w, false, true, false)) != MOE_OK) return s;
+  if (T > 0 && (!x || !topk_idx || !perm || !offsets || !y)) return MOE_ERR_NULL;
+  if (T > 0 && dims->n_shared > 0 && !shared_y) return MOE_ERR_NULL;
+  if (misaligned(x) || misaligned(y) || misaligned(shared_y)) return MOE_ERR_SHAPE;
+  Layout L = make_layout(dims, T);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  return do_experts(dims, w, x, T, topk_idx, perm, offsets, y, shared_y, ws, L,
+                    (hipStream_t)stream);
+}
+
+int32_t moe_combine(const moe_dims* dims, const moe_weights* w, const void* x, int64_t T,
+                    const int32_t* topk_idx, const float* topk_gate, const int32_t* inv_perm,
+                    const void* y, const void* shared_y, void* out, moe_stream stream) {
+  int32_t s = validate_dims(dims, T);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(dims, w, false, false, true)) != MOE_OK) return s;
+  if (T > 0 && (!x || !topk_idx || !topk_gate || !inv_perm || !y || !out)) return MOE_ERR_NULL;
+  if (T > 0 && dims->n_shared > 0 && !shared_y) return MOE_ERR_NULL;
+  if (misaligned(x) || misaligned(y) || misaligned(shared_y) || misaligned(out))
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  return do_combine(dims, w, x, T, topk_idx, topk_gate, inv_perm, y, shared_y, out,
+                    (hipStream_t)stream);
+}
+
+int32_t moe_forward(const moe_dims* dims, const moe_weights* w, const void* x, int64_t T,
+                    void* out, int32_t* topk_idx_opt, float* topk_gate_opt, void* ws,
+                    size_t ws_bytes, moe_stream stream) {
+  int32_t s = validate_dims(dims, T);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(dims, w, true, true, true)) != MOE_OK) return s;
+  if (T > 0 && (!x || !out)) return MOE_ERR_NULL;
+  if (misaligned(x) || misaligned(out)) return MOE_ERR_SHAPE;
+  Layout L = make_layout(dims, T);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* idx = topk_idx_opt ? topk_idx_opt : at<int32_t*>(ws, L.idx);
+  float* gate = topk_gate_opt ? topk_gate_opt : at<float*>(ws, L.gate);
+  int32_t* counts = at<int32_t*>(ws, L.counts);
+  int32_t* offsets = at<int32_t*>(ws, L.offsets);
+  int32_t* perm = at<int32_t*>(ws, L.perm);
+  int32_t* inv = at<int32_t*>(ws, L.inv);
+  void* y = at<void*>(ws, L.y);
+  void* sy = dims->n_shared ? at<void*>(ws, L.sy) : nullptr;
+  if ((s = do_route(dims, w, x, T, idx, gate, ws, L, st)) != MOE_OK) return s;
+  MOE_TRY(launch_dispatch(idx, L.n, dims->E, counts, offsets, perm, inv,
+                          at<int32_t*>(ws, L.disp), st));
+  if ((s = do_experts(dims, w, x, T, idx, perm, offsets, y, sy, ws, L, st)) != MOE_OK) return s;
+  return do_combine(dims, w, x, T, idx, gate, inv, y, sy, out, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,344 @@
+// Grouped GEMMs of the expert stage ("OmniMoE: An Efficient MoE by
+// Orchestrating Atomic Experts at Scale", Technical Summary sec. 2.2, step
+// Grouped GEMM: a block of expert weights is loaded once and reused across
+// all tokens of the expert's group).
+//
+//   GEMM1 (+ fused SiLU gate):  H = silu(X_e W_gate,e^T) * (X_e W_up,e^T)
+//   GEMM2:                      Y = H_e W_down,e^T
+//
+// X_e rows are gathered from x through the dispatch permutation while the
+// A tile is loaded.  Shared experts are extra groups whose rows are all
+// tokens in order.
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A block tile
+// is BM x BN (B rows) x 64 (K) staged through LDS, double buffered; every
+// 16-byte chunk of a 128-byte LDS row is stored at chunk ^ (row & 7) so the
+// MFMA fragment reads of 8 consecutive rows hit distinct banks.  For GEMM1
+// the B tile holds BN/2 W_gate rows and the same BN/2 W_up rows, and each
+// wave's fragments pair gate and up columns, so silu(g)*u is formed in
+// registers and H is written once, in bf16.
+#include "kernels.h"
+
+namespace moe {
+
+
+template <bool SWIGLU>
+struct TileCtx {
+  bool shared;
+  int e;      // expert index inside its table
+  int64_t r0; // first row in the group's row space
+  int nr;     // valid rows
+  int N, K;
+};
+
+template <bool SWIGLU>
+__device__ __forceinline__ TileCtx<SWIGLU> tile_ctx(const GemmArgs& a, int4 t) {
+  TileCtx<SWIGLU> c;
+  c.shared = t.x >= a.E_ffn;
+  c.e = c.shared ? t.x - a.E_ffn : t.x;
+  c.r0 = t.y;
+  c.nr = t.z;
+  c.N = c.shared ? a.N_shared : a.N_routed;
+  c.K = c.shared ? a.K_shared : a.K_routed;
+  return c;
+}
+
+// A row source (element pointer) of local row i, or nullptr when out of range
+template <typename T, bool SWIGLU>
+__device__ __forceinline__ const T* a_row(const GemmArgs& a, const TileCtx<SWIGLU>& c, int i) {
+  if (i >= c.nr) return nullptr;
+  const int64_t r = c.r0 + i;
+  if (SWIGLU) {
+    int64_t tok = c.shared ? r : (int64_t)(a.perm[r] / a.k);
+    return reinterpret_cast<const T*>(a.a_x) + tok * c.K;
+  }
+  if (c.shared)
+    return reinterpret_cast<const T*>(a.a_shared) + ((int64_t)c.e * a.T + r) * c.K;
+  return reinterpret_cast<const T*>(a.a_routed) + r * c.K;
+}
+
+// B row source of tile row j (0 <= j < BN), or nullptr past N
+template <typename T, bool SWIGLU, int BN>
+__device__ __forceinline__ const T* b_row(const GemmArgs& a, const TileCtx<SWIGLU>& c, int n0,
+                                          int j) {
+  const void* base;
+  int n;
+  if (SWIGLU) {
+    const bool up = j >= BN / 2;
+    n = n0 + (up ? j - BN / 2 : j);
+    base = c.shared ? (up ? a.b1_shared : a.b0_shared) : (up ? a.b1_routed : a.b0_routed);
+  } else {
+    n = n0 + j;
+    base = c.shared ? a.b0_shared : a.b0_routed;
+  }
+  if (n >= c.N) return nullptr;
+  return reinterpret_cast<const T*>(base) + ((int64_t)c.e * c.N + n) * c.K;
+}
+
+template <typename T, bool SWIGLU>
+__device__ __forceinline__ T* c_row(const GemmArgs& a, const TileCtx<SWIGLU>& c, int i) {
+  const int64_t r = c.r0 + i;
+  if (c.shared) return reinterpret_cast<T*>(a.c_shared) + ((int64_t)c.e * a.T + r) * c.N;
+  return reinterpret_cast<T*>(a.c_routed) + r * c.N;
+}
+
+// ------------------------------------------------------------------------
+// bf16 MFMA grouped GEMM.  WM x WN waves, each FM x FN 32x32 fragments.
+template <int WM, int WN, int FM, int FN, bool SWIGLU>
+__global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs args) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BM = WM * FM * 32;
+  constexpr int BN = WN * FN * 32;
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;  // output columns per tile
+  constexpr int BK = 64;
+  constexpr int CA = BM * 8 / NT;  // 16-byte chunks per thread per K tile
+  constexpr int CB = BN * 8 / NT;
+  static_assert(CA >= 1 && CB >= 1 && (NT / 8) % 8 == 0, "tile shape");
+  static_assert(!SWIGLU || FN % 2 == 0, "gate/up pairs");
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * BK];
+
+  const int tile_id = blockIdx.x;
+  if (tile_id >= *args.ntiles) return;
+  const int4 tl = args.tiles[tile_id];
+  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl);
+  const int n0 = blockIdx.y * BNO;
+  if (n0 >= c.N) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // loader: this thread's rows are (tid >> 3) + (NT/8) i, chunk tid & 7
+  const int lrow = tid >> 3;
+  const int lchunk = tid & 7;
+  const int lphys = (lchunk ^ (lrow & 7)) * 8;
+  const uint16_t* ap[CA];
+  const uint16_t* bp[CB];
+#pragma unroll
+  for (int i = 0; i < CA; i++) ap[i] = a_row<uint16_t, SWIGLU>(args, c, lrow + (NT / 8) * i);
+#pragma unroll
+  for (int i = 0; i < CB; i++) bp[i] = b_row<uint16_t, SWIGLU, BN>(args, c, n0, lrow + (NT / 8) * i);
+
+  u32x4 ra[CA], rb[CB];
+  auto gload = [&](int kt) {
+    const int col = kt * BK + lchunk * 8;
+#pragma unroll
+    for (int i = 0; i < CA; i++)
+      ra[i] = ap[i] ? *reinterpret_cast<const u32x4*>(ap[i] + col) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < CB; i++)
+      rb[i] = bp[i] ? *reinterpret_cast<const u32x4*>(bp[i] + col) : u32x4{0, 0, 0, 0};
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; i++)
+      *reinterpret_cast<u32x4*>(&lds_a[buf][(lrow + (NT / 8) * i) * BK + lphys]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < CB; i++)
+      *reinterpret_cast<u32x4*>(&lds_b[buf][(lrow + (NT / 8) * i) * BK + lphys]) = rb[i];
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++) acc[i][j] = f32x16{};
+
+  // fragment row bases inside the tile
+  int brow[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; fn++) {
+    if (SWIGLU) {
+      const int half = FN / 2;
+      brow[fn] = (fn < half) ? (wn * half + fn) * 32 : BN / 2 + (wn * half + fn - half) * 32;
+    } else {
+      brow[fn] = (wn * FN + fn) * 32;
+    }
+  }
+  const int frow = lane & 31;
+  const int fsw = lane & 7;
+  const int fhalf = lane >> 5;
+
+  const int nk = c.K / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt++) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int s = 0; s < BK / 16; s++) {
+      const int ch = ((2 * s + fhalf) ^ fsw) * 8;
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; fm++)
+        af[fm] = *reinterpret_cast<const bf16x8*>(
+            &lds_a[cur][((wm * FM + fm) * 32 + frow) * BK + ch]);
+#pragma unroll
+      for (int fn = 0; fn < FN; fn++)
+        bfr[fn] = *reinterpret_cast<const bf16x8*>(&lds_b[cur][(brow[fn] + frow) * BK + ch]);
+#pragma unroll
+      for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds C[8(j/4) + 4(l/32) + j%4][l%32] of each fragment
+  const int ccol = lane & 31;
+#pragma unroll
+  for (int fm = 0; fm < FM; fm++) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int row = (wm * FM + fm) * 32 + 8 * (j >> 2) + 4 * fhalf + (j & 3);
+      if (row >= c.nr) continue;
+      uint16_t* out = c_row<uint16_t, SWIGLU>(args, c, row);
+      if (SWIGLU) {
+        const int half = FN / 2;
+#pragma unroll
+        for (int fn = 0; fn < half; fn++) {
+          const int col = n0 + (wn * half + fn) * 32 + ccol;
+          const float g = acc[fm][fn][j], u = acc[fm][fn + half][j];
+          if (col < c.N) out[col] = f32_to_bf16(silu_f32(g) * u);
+        }
+      } else {
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+          const int col = n0 + (wn * FN + fn) * 32 + ccol;
+          if (col < c.N) out[col] = f32_to_bf16(acc[fm][fn][j]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// fp32 layers: plain FMA, one thread per output element, 32-row tiles.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
+  const int tile_id = blockIdx.x;
+  if (tile_id >= *args.ntiles) return;
+  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
+  const int n0 = blockIdx.y * 64;
+  if (n0 >= c.N) return;
+  const int i = threadIdx.x >> 3;  // local row 0..31
+  if (i >= c.nr) return;
+  const float* a = a_row<float, SWIGLU>(args, c, i);
+  float* out = c_row<float, SWIGLU>(args, c, i);
+  for (int jj = threadIdx.x & 7; jj < 64; jj += 8) {
+    const int n = n0 + jj;
+    if (n >= c.N) break;
+    if (SWIGLU) {
+      const float* g = b_row<float, SWIGLU, 2>(args, c, n, 0);
+      const float* u = b_row<float, SWIGLU, 2>(args, c, n, 1);
+      float sg = 0.f, su = 0.f;
+      for (int kk = 0; kk < c.K; kk++) {
+        sg = fmaf(a[kk], g[kk], sg);
+        su = fmaf(a[kk], u[kk], su);
+      }
+      out[n] = silu_f32(sg) * su;
+    } else {
+      const float* b = b_row<float, SWIGLU, 1>(args, c, n, 0);
+      float s = 0.f;
+      for (int kk = 0; kk < c.K; kk++) s = fmaf(a[kk], b[kk], s);
+      out[n] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Tile list: routed experts e < E_ffn get ceil(count_e / BM) tiles of
+// sorted positions; shared expert s gets ceil(T / BM) tiles of tokens.
+// Single block; E_ffn <= 1024.
+__global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ offsets,
+                                                      int E_ffn, int n_shared, int64_t T, int BM,
+                                                      int4* __restrict__ tiles,
+                                                      int32_t* __restrict__ ntiles) {
+  __shared__ int32_t pre[1024];
+  const int e = threadIdx.x;
+  const int cnt = e < E_ffn ? offsets[e + 1] - offsets[e] : 0;
+  const int nt = (cnt + BM - 1) / BM;
+  pre[e] = nt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int v = e >= o ? pre[e - o] : 0;
+    __syncthreads();
+    pre[e] += v;
+    __syncthreads();
+  }
+  const int start = pre[e] - nt;
+  const int routed_total = pre[1023];
+  if (e < E_ffn) {
+    const int base = offsets[e];
+    for (int i = 0; i < nt; i++) {
+      const int r = i * BM;
+      tiles[start + i] = make_int4(e, base + r, cnt - r < BM ? cnt - r : BM, 0);
+    }
+  }
+  const int per_shared = (int)((T + BM - 1) / BM);
+  for (int j = e; j < n_shared * per_shared; j += 1024) {
+    const int s = j / per_shared, i = j % per_shared;
+    const int r = i * BM;
+    tiles[routed_total + j] = make_int4(E_ffn + s, r, (int)(T - r < BM ? T - r : BM), 0);
+  }
+  if (e == 0) *ntiles = routed_total + n_shared * per_shared;
+}
+
+// ------------------------------------------------------------------------
+// launchers
+
+int gemm_tile_rows(int dtype, int64_t tasks, int E_ffn) {
+  if (dtype != MOE_BF16) return 32;
+  // small groups (decode-sized batches): 32-row tiles; otherwise 256
+  return (E_ffn > 0 && tasks / E_ffn < 64) ? 32 : 256;
+}
+
+int64_t gemm_max_tiles(int64_t T, int k, int E_ffn, int n_shared, int BM) {
+  return cdiv(T * k, BM) + E_ffn + n_shared * cdiv(T, BM);
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E_ffn,
+                              int n_shared, int64_t T, int BM, int4* tiles, int32_t* ntiles,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, st, offsets, E_ffn, n_shared,
+                     T, BM, tiles, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a,
+                               int64_t max_tiles, hipStream_t st) {
+  const int Nmax = a.N_routed > a.N_shared ? a.N_routed : a.N_shared;
+  if (max_tiles == 0 || Nmax == 0) return hipSuccess;
+  if (dtype == MOE_F32) {
+    dim3 grid((unsigned)max_tiles, (unsigned)cdiv(Nmax, 64));
+    if (swiglu)
+      hipLaunchKernelGGL(k_grouped_gemm_f32<true>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_grouped_gemm_f32<false>, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  if (BM == 256) {
+    constexpr int BN = 256;
+    const int bno = swiglu ? BN / 2 : BN;
+    dim3 grid((unsigned)max_tiles, (unsigned)cdiv(Nmax, bno));
+    if (swiglu)
+      hipLaunchKernelGGL((k_grouped_gemm_bf16<2, 2, 4, 4, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_grouped_gemm_bf16<2, 2, 4, 4, false>), grid, dim3(256), 0, st, a);
+  } else {
+    constexpr int BN = 256;
+    const int bno = swiglu ? BN / 2 : BN;
+    dim3 grid((unsigned)max_tiles, (unsigned)cdiv(Nmax, bno));
+    if (swiglu)
+      hipLaunchKernelGGL((k_grouped_gemm_bf16<1, 4, 1, 2, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_grouped_gemm_bf16<1, 4, 1, 2, false>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,83 @@
+// Internal launchers of the gfx950 MoE kernels (not part of the C ABI).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct GemmArgs {
+  const int4* tiles;       // {group, first row, rows, 0}
+  const int32_t* ntiles;   // device count of valid tiles
+  int E_ffn;
+  int64_t T;
+  // A operand
+  const void* a_x;         // GEMM1: x [T, d], rows gathered
+  const int32_t* perm;     // GEMM1 routed rows: token = perm[p] / k
+  int k;
+  const void* a_routed;    // GEMM2: H rows of routed tasks [*, f]
+  const void* a_shared;    // GEMM2: H rows of shared experts [n_shared*T, f_shared]
+  // B operand, [groups, N, K] each
+  const void* b0_routed;
+  const void* b1_routed;
+  const void* b0_shared;
+  const void* b1_shared;
+  // C
+  void* c_routed;
+  void* c_shared;
+  int N_routed, N_shared;  // output columns
+  int K_routed, K_shared;
+};
+
+struct CombineArgs {
+  const void* x;
+  const int32_t* idx;
+  const float* gate;
+  const int32_t* inv_perm;
+  const void* y;
+  const void* shared_y;
+  void* out;
+  const float* const_wc;
+  const void* const_v;
+  int64_t T;
+  int d, k, E_ffn, n_shared;
+  int zc_kind[MOE_MAX_ZC];
+  int const_index[MOE_MAX_ZC];
+};
+
+// router.hip
+hipError_t launch_split_router(const float* W, uint16_t* W3, int64_t n, hipStream_t st);
+hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, int x_off,
+                                const void* W, int64_t slice, int NL, int K, float* logits,
+                                int ldl, int col_off, hipStream_t st);
+hipError_t launch_select_topk(const float* logits, int64_t T, int E, int E_ffn, int k, float tau,
+                              const float* bias, int renorm, int32_t* idx, float* gate,
+                              hipStream_t st);
+hipError_t launch_select_pk(const float* scores, int64_t T, int rows, int cols, int krow, int kcol,
+                            int k, int32_t* idx, float* gate, hipStream_t st);
+
+// dispatch.hip
+int64_t dispatch_scratch_ints(int64_t n, int E);
+hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* scratch,
+                           hipStream_t st);
+
+// gemm.hip
+int gemm_tile_rows(int dtype, int64_t tasks, int E_ffn);
+int64_t gemm_max_tiles(int64_t T, int k, int E_ffn, int n_shared, int BM);
+hipError_t launch_build_tiles(const int32_t* offsets, int E_ffn,
+                              int n_shared, int64_t T, int BM, int4* tiles, int32_t* ntiles,
+                              hipStream_t st);
+hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a,
+                               int64_t max_tiles, hipStream_t st);
+
+// combine.hip
+hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t st);
+hipError_t launch_atomic_h(int dtype, const void* x, const void* atom_u, const int32_t* idx,
+                           const int32_t* perm, int64_t n, int k, int d, float* h,
+                           hipStream_t st);
+hipError_t launch_atomic_combine(int dtype, const void* atom_w, const int32_t* idx,
+                                 const float* gate, const int32_t* inv_perm, const float* h,
+                                 const void* shared_y, int n_shared, int64_t T, int k, int d,
+                                 void* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,318 @@
+// Router kernels: logits (fp32-exact dot products on bf16 MFMA, or plain
+// fp32 FMA for fp32 layers) and the per-token selection (softmax top-k, or
+// the Cartesian-product candidate search).
+//
+// Routing follows "OmniMoE: An Efficient MoE by Orchestrating Atomic Experts
+// at Scale" (Technical Summary sec. 1: a router over N experts costs O(N d);
+// sec. 2.2 "Cartesian Product Router": row and column logits over a 2-D
+// expert grid, combined to score experts) and the MoE++ page ("Approach":
+// one router over FFN and zero-computation experts, tau on the FFN ones).
+#include "kernels.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------
+// fp32 router weights -> three bf16 slices (hi + mid + lo == w exactly).
+//
+// hi keeps the top 8 significant bits of w (truncation), mid the next 8 of
+// the exact remainder w - hi, and lo the remaining <= 8 bits, which bf16
+// holds exactly.  A bf16 x times each slice is exact in fp32, so three bf16
+// MFMA passes with fp32 accumulation give an fp32-accurate dot product at
+// matrix-core rate.  Layout: W3[p][n][kk], p = 0..2.
+__global__ void k_split_router(const float* __restrict__ W, uint16_t* __restrict__ W3, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = W[i];
+  uint32_t hb = __float_as_uint(v) & 0xffff0000u;
+  float r1 = v - __uint_as_float(hb);
+  uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+  float r2 = r1 - __uint_as_float(mb);
+  W3[i] = (uint16_t)(hb >> 16);
+  W3[n + i] = (uint16_t)(mb >> 16);
+  W3[2 * n + i] = (uint16_t)(__float_as_uint(r2) >> 16);  // exact: <= 8 bits left
+}
+
+// ------------------------------------------------------------------------
+// logits[t, col_off + n] = x[t, x_off : x_off+K] . W[n, :K]   (n < NL)
+// bf16 x, W given as the three bf16 slices W3[p * slice + n * K + kk].
+// Block: 4 waves in a 2x2 grid, each wave one 32x32 MFMA tile; grid
+// (ceil(T/64), ceil(NL/64)).  Operands go straight from global memory to
+// MFMA registers: per 32-wide K block, lane (r = l%32, q = l/32) loads 16
+// consecutive elements of its row at q*16, and MFMA step s uses elements
+// [q*16 + 8s, +8).  A and B use the same K permutation, so the dot products
+// are unchanged while every row is read as one 64-byte run.
+__global__ __launch_bounds__(256) void k_router_logits_bf16(
+    const uint16_t* __restrict__ x, int64_t T, int ldx, int x_off,
+    const uint16_t* __restrict__ W3, int64_t slice, int NL, int K,
+    float* __restrict__ logits, int ldl, int col_off) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * 64 + (wave >> 1) * 32;
+  const int n0 = blockIdx.y * 64 + (wave & 1) * 32;
+  const int r = lane & 31, q = lane >> 5;
+  const int64_t am = m0 + r;
+  const int bn = n0 + r;
+  const bool a_ok = am < T, b_ok = bn < NL;
+  const uint16_t* ap = x + (a_ok ? am : 0) * (int64_t)ldx + x_off + q * 16;
+  const uint16_t* bp = W3 + (int64_t)(b_ok ? bn : 0) * K + q * 16;
+  f32x16 acc = {};
+  for (int kb = 0; kb < K; kb += 32) {
+    u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+    if (a_ok) {
+      a0 = *reinterpret_cast<const u32x4*>(ap + kb);
+      a1 = *reinterpret_cast<const u32x4*>(ap + kb + 8);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; p++) {
+      u32x4 b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+      if (b_ok) {
+        b0 = *reinterpret_cast<const u32x4*>(bp + p * slice + kb);
+        b1 = *reinterpret_cast<const u32x4*>(bp + p * slice + kb + 8);
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                    __builtin_bit_cast(bf16x8, b0), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                    __builtin_bit_cast(bf16x8, b1), acc, 0, 0, 0);
+    }
+  }
+  const int n = n0 + r;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    int64_t m = m0 + 8 * (j >> 2) + 4 * q + (j & 3);
+    if (m < T && n < NL) logits[m * ldl + col_off + n] = acc[j];
+  }
+}
+
+// fp32 layers: one thread per logit, four interleaved fp32 partial sums.
+__global__ void k_router_logits_f32(const float* __restrict__ x, int64_t T, int ldx, int x_off,
+                                    const float* __restrict__ W, int NL, int K,
+                                    float* __restrict__ logits, int ldl, int col_off) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * NL) return;
+  int64_t t = i / NL;
+  int n = (int)(i % NL);
+  const float* a = x + t * ldx + x_off;
+  const float* b = W + (int64_t)n * K;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  for (int kk = 0; kk < K; kk += 4) {
+    s0 = fmaf(a[kk], b[kk], s0);
+    s1 = fmaf(a[kk + 1], b[kk + 1], s1);
+    s2 = fmaf(a[kk + 2], b[kk + 2], s2);
+    s3 = fmaf(a[kk + 3], b[kk + 3], s3);
+  }
+  logits[t * ldl + col_off + n] = (s0 + s1) + (s2 + s3);
+}
+
+// ------------------------------------------------------------------------
+// Softmax top-k selection, one wave per token.  V = values per lane
+// (E <= 64 V).  Logit l = fl32(dot + bias), then fl32(tau * l) for FFN
+// experts.  Order (-l, e); gates = softmax over all E at the chosen ones,
+// optionally renormalised over the k.
+template <int V>
+__global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ logits, int64_t T,
+                                                    int E, int E_ffn, int k, float tau,
+                                                    const float* __restrict__ bias, int renorm,
+                                                    int32_t* __restrict__ idx_out,
+                                                    float* __restrict__ gate_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; i++) {
+    int e = lane + 64 * i;
+    float l = -INFINITY;
+    if (e < E) {
+      l = row[e];
+      if (bias) l = l + bias[e];
+      if (e < E_ffn) l = tau * l;
+    }
+    v[i] = l;
+  }
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < V; i++) m = fmaxf(m, v[i]);
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; i++)
+    if (lane + 64 * i < E) s += __expf(v[i] - m);
+  s = wave_sum(s);
+  uint32_t taken = 0;
+  float my_val = 0.f;
+  int my_idx = 0;
+  float gsum = 0.f;
+  for (int j = 0; j < k; j++) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+      int e = lane + 64 * i;
+      bool ok = e < E && !((taken >> i) & 1u);
+      if (ok && (v[i] > bv || bi == 0x7fffffff)) { bv = v[i]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    float g = __expf(bv - m) / s;
+    gsum += g;
+    if (lane == j) { my_val = g; my_idx = bi; }
+  }
+  if (lane < k) {
+    float g = renorm ? my_val / gsum : my_val;
+    idx_out[t * k + lane] = my_idx;
+    gate_out[t * k + lane] = g;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Cartesian-product selection, one wave per token.
+//   scores: [T, rows + cols] (row scores first).
+//   1. top-krow rows, top-kcol columns by (-score, index);
+//   2. candidates (a, b): sigma = fl32(s_r + s_c), id = row * cols + col;
+//   3. top-k candidates by (-sigma, id); gates = softmax over the k sigmas.
+// V = values per lane (max(rows, cols, krow*kcol) <= 64 V); krow, kcol <= 64.
+template <int V>
+__global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ scores, int64_t T,
+                                                  int rows, int cols, int krow, int kcol, int k,
+                                                  int32_t* __restrict__ idx_out,
+                                                  float* __restrict__ gate_out) {
+  __shared__ float sel_val[4][2][64];
+  __shared__ int sel_idx[4][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float* srow = scores + t * (int64_t)(rows + cols);
+  // steps 1: rows then columns
+  for (int side = 0; side < 2; side++) {
+    const int n = side ? cols : rows;
+    const int kk = side ? kcol : krow;
+    const float* s = srow + (side ? rows : 0);
+    float v[V];
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+      int e = lane + 64 * i;
+      v[i] = e < n ? s[e] : -INFINITY;
+    }
+    uint32_t taken = 0;
+    for (int j = 0; j < kk; j++) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < V; i++) {
+        int e = lane + 64 * i;
+        bool ok = e < n && !((taken >> i) & 1u);
+        if (ok && (v[i] > bv || bi == 0x7fffffff)) { bv = v[i]; bi = e; }
+      }
+      wave_argmax(bv, bi);
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == 0) { sel_val[wave][side][j] = bv; sel_idx[wave][side][j] = bi; }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // step 2: candidate scores
+  const int nc = krow * kcol;
+  float v[V];
+  int id[V];
+#pragma unroll
+  for (int i = 0; i < V; i++) {
+    int c = lane + 64 * i;
+    if (c < nc) {
+      int a = c / kcol, b = c - a * kcol;
+      v[i] = sel_val[wave][0][a] + sel_val[wave][1][b];
+      id[i] = sel_idx[wave][0][a] * cols + sel_idx[wave][1][b];
+    } else {
+      v[i] = -INFINITY;
+      id[i] = 0x7fffffff;
+    }
+  }
+  // step 3: top-k candidates
+  uint32_t taken = 0;
+  float top = 0.f, my_val = 0.f;
+  int my_id = 0;
+  float gsum = 0.f;
+  for (int j = 0; j < k; j++) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff, bslot = 0;
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+      bool ok = (lane + 64 * i) < nc && !((taken >> i) & 1u);
+      if (ok && (v[i] > bv || (v[i] == bv && id[i] < bi))) { bv = v[i]; bi = id[i]; bslot = i; }
+    }
+    int owner_key = bi;
+    wave_argmax(bv, bi);
+    if (owner_key == bi && bi != 0x7fffffff) {
+      // the lane holding the winner marks it (ids are unique)
+      taken |= 1u << bslot;
+    }
+    if (j == 0) top = bv;
+    float e = __expf(bv - top);
+    gsum += e;
+    if (lane == j) { my_val = e; my_id = bi; }
+  }
+  if (lane < k) {
+    idx_out[t * k + lane] = my_id;
+    gate_out[t * k + lane] = my_val / gsum;
+  }
+}
+
+// ------------------------------------------------------------------------
+// launchers
+
+hipError_t launch_split_router(const float* W, uint16_t* W3, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_split_router, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, W, W3, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, int x_off,
+                                const void* W, int64_t slice, int NL, int K, float* logits,
+                                int ldl, int col_off, hipStream_t st) {
+  if (T == 0 || NL == 0) return hipSuccess;
+  if (dtype == MOE_BF16) {
+    dim3 grid((unsigned)cdiv(T, 64), (unsigned)cdiv(NL, 64));
+    hipLaunchKernelGGL(k_router_logits_bf16, grid, dim3(256), 0, st, (const uint16_t*)x, T, ldx,
+                       x_off, (const uint16_t*)W, slice, NL, K, logits, ldl, col_off);
+  } else {
+    hipLaunchKernelGGL(k_router_logits_f32, dim3((unsigned)cdiv(T * NL, 256)), dim3(256), 0, st,
+                       (const float*)x, T, ldx, x_off, (const float*)W, NL, K, logits, ldl,
+                       col_off);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_topk(const float* logits, int64_t T, int E, int E_ffn, int k, float tau,
+                              const float* bias, int renorm, int32_t* idx, float* gate,
+                              hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(T, 4)), block(256);
+  int V = (int)cdiv(E, 64);
+#define SEL(VV) hipLaunchKernelGGL(k_select_topk<VV>, grid, block, 0, st, logits, T, E, E_ffn, k, \
+                                   tau, bias, renorm, idx, gate)
+  if (V <= 1) SEL(1);
+  else if (V <= 2) SEL(2);
+  else SEL(4);
+#undef SEL
+  return hipGetLastError();
+}
+
+hipError_t launch_select_pk(const float* scores, int64_t T, int rows, int cols, int krow, int kcol,
+                            int k, int32_t* idx, float* gate, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  int64_t mx = rows;
+  if (cols > mx) mx = cols;
+  if ((int64_t)krow * kcol > mx) mx = (int64_t)krow * kcol;
+  int V = (int)cdiv(mx, 64);
+  dim3 grid((unsigned)cdiv(T, 4)), block(256);
+#define SEL(VV) hipLaunchKernelGGL(k_select_pk<VV>, grid, block, 0, st, scores, T, rows, cols, krow, \
+                                   kcol, k, idx, gate)
+  if (V <= 1) SEL(1);
+  else if (V <= 2) SEL(2);
+  else if (V <= 4) SEL(4);
+  else if (V <= 8) SEL(8);
+  else SEL(16);
+#undef SEL
+  return hipGetLastError();
+}
+
+}  // namespace moe

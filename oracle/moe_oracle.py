@@ -326,14 +326,14 @@ def forward(cfg, inp, idx=None, gate=None, tokens=None):
         perm_use, inv_use, off_use = perm, inv_perm, offsets
     if cfg.router == 1:
         Y = atomic_h(cfg, inp, idx, perm_use)
-        SY = np.zeros((0, cfg.d))
     else:
         Y, _ = expert_ffn(cfg.replace(n_shared=0), inp, idx, perm_use, off_use)
-        rows = np.arange(T) if tokens is None else tokens
-        SY = np.zeros((cfg.n_shared * T, cfg.d))
-        x64 = as_f64(inp["x"])[rows]
-        for s in range(cfg.n_shared):
-            SY[s * T + rows] = swiglu(x64, inp["shared_gate"][s],
-                                      inp["shared_up"][s], inp["shared_down"][s])
+    # shared dense experts, always active ([OMNI] sec. 2.1 "Shared Dense MLP")
+    rows = np.arange(T) if tokens is None else tokens
+    SY = np.zeros((cfg.n_shared * T, cfg.d))
+    x64 = as_f64(inp["x"])[rows]
+    for s in range(cfg.n_shared):
+        SY[s * T + rows] = swiglu(x64, inp["shared_gate"][s],
+                                  inp["shared_up"][s], inp["shared_down"][s])
     out = combine(cfg, inp, idx, gate, inv_use, Y, SY, tokens)
     return out, idx, gate

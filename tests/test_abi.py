@@ -1,0 +1,176 @@
+"""The C-ABI library loads, exports every symbol include/moe.h declares, and
+rejects bad arguments on the host before any GPU call (no device needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_22_amd import binding as B
+from mixture_experts_layer_22_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = 0x10000000  # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe_mi355x.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert isinstance(B.status_str(s), str) and B.status_str(s)
+    assert B.status_str(99) == "unknown status"
+
+
+def _dims(name="deepseek16b", **kw):
+    cfg = I.CONFIGS[name].replace(**kw)
+    return B.dims_from_config(cfg)
+
+
+def _ws_size(dims, T):
+    n = ctypes.c_size_t(0)
+    return B.load().moe_workspace_size(ctypes.byref(dims), T, ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("name", I.CONFIG_ORDER)
+def test_workspace_size_valid_configs(lib, name):
+    dims = B.dims_from_config(I.CONFIGS[name])
+    s, n1 = _ws_size(dims, 16)
+    assert s == B.MOE_OK and n1 > 0
+    s, n2 = _ws_size(dims, I.CONFIGS[name].T)
+    assert s == B.MOE_OK and n2 >= n1
+    assert _ws_size(dims, 0)[0] == B.MOE_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=100), B.MOE_ERR_SHAPE),
+    (dict(d=0), B.MOE_ERR_SHAPE),
+    (dict(k=65), B.MOE_ERR_SHAPE),
+    (dict(k=0), B.MOE_ERR_SHAPE),
+    (dict(E=4, E_ffn=4, k=6), B.MOE_ERR_SHAPE),
+    (dict(f=100), B.MOE_ERR_SHAPE),
+    (dict(E=300, E_ffn=300), B.MOE_ERR_SHAPE),
+    (dict(n_shared=2, f_shared=10), B.MOE_ERR_SHAPE),
+    (dict(E=80, E_ffn=64), B.MOE_ERR_SHAPE),          # 16 zero-computation experts > 8
+    (dict(router=5), B.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_dims_rejected(lib, kw, status):
+    dims = _dims(**kw)
+    assert _ws_size(dims, 8)[0] == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k=300),                                   # k > k_row * k_col
+    dict(pk_k_row=65),
+    dict(pk_rows=128),                             # rows * cols != E
+    dict(E_ffn=3),
+])
+def test_bad_product_key_dims(lib, kw):
+    dims = _dims("atomic-pk", **kw)
+    assert _ws_size(dims, 8)[0] == B.MOE_ERR_SHAPE
+
+
+def test_bad_dtype(lib):
+    dims = _dims()
+    dims.dtype = 7
+    assert _ws_size(dims, 8)[0] == B.MOE_ERR_DTYPE
+
+
+def test_bad_zc_kind(lib):
+    dims = _dims("moepp")
+    dims.zc_kind[1] = 9
+    assert _ws_size(dims, 8)[0] == B.MOE_ERR_SHAPE
+
+
+def test_negative_T_and_null_dims(lib):
+    dims = _dims()
+    assert _ws_size(dims, -1)[0] == B.MOE_ERR_SHAPE
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(None, 8, ctypes.byref(n)) == B.MOE_ERR_NULL
+    assert lib.moe_workspace_size(ctypes.byref(dims), 8, None) == B.MOE_ERR_NULL
+
+
+def _weights(**over):
+    w = B.MoeWeights()
+    for f, _ in B.MoeWeights._fields_:
+        setattr(w, f, FAKE)
+    for k, v in over.items():
+        setattr(w, k, v)
+    return w
+
+
+def test_null_pointers_rejected(lib):
+    dims = _dims()
+    _, need = _ws_size(dims, 8)
+    w = _weights()
+    P = FAKE
+    # missing router weights
+    assert lib.moe_route(ctypes.byref(dims), ctypes.byref(_weights(router_w=None)), P, 8, P, P,
+                         P, need, None) == B.MOE_ERR_NULL
+    # missing outputs
+    assert lib.moe_route(ctypes.byref(dims), ctypes.byref(w), P, 8, None, P, P, need,
+                         None) == B.MOE_ERR_NULL
+    # missing expert weights
+    assert lib.moe_expert_ffn(ctypes.byref(dims), ctypes.byref(_weights(w_down=None)), P, 8, P,
+                              P, P, P, P, P, need, None) == B.MOE_ERR_NULL
+    # shared experts configured but no shared output
+    assert lib.moe_expert_ffn(ctypes.byref(dims), ctypes.byref(w), P, 8, P, P, P, P, None, P,
+                              need, None) == B.MOE_ERR_NULL
+    assert lib.moe_dispatch(ctypes.byref(dims), P, 8, None, P, P, P, P, need,
+                            None) == B.MOE_ERR_NULL
+    assert lib.moe_combine(ctypes.byref(dims), ctypes.byref(w), P, 8, P, P, P, P, P, None,
+                           None) == B.MOE_ERR_NULL
+    assert lib.moe_forward(ctypes.byref(dims), ctypes.byref(w), None, 8, P, None, None, P, need,
+                           None) == B.MOE_ERR_NULL
+    # constant experts need W_c and v in the combine
+    d4 = _dims("moepp")
+    assert lib.moe_combine(ctypes.byref(d4), ctypes.byref(_weights(const_v=None)), P, 8, P, P,
+                           P, P, P, P, None) == B.MOE_ERR_NULL
+
+
+def test_workspace_too_small_and_misaligned(lib):
+    dims = _dims()
+    _, need = _ws_size(dims, 8)
+    w = _weights()
+    P = FAKE
+    assert lib.moe_forward(ctypes.byref(dims), ctypes.byref(w), P, 8, P, None, None, P,
+                           need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(dims), ctypes.byref(w), P, 8, P, P, P, 0,
+                         None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(ctypes.byref(dims), ctypes.byref(w), P + 8, 8, P, None, None, P, need,
+                           None) == B.MOE_ERR_SHAPE
+    assert lib.moe_forward(ctypes.byref(dims), ctypes.byref(w), P, 8, P, None, None, P + 16,
+                           need, None) == B.MOE_ERR_SHAPE
+
+
+def test_T_zero_is_noop(lib):
+    dims = _dims()
+    w = _weights()
+    _, need = _ws_size(dims, 0)
+    P = FAKE
+    # T = 0 returns before any GPU call, even with no outputs
+    assert lib.moe_forward(ctypes.byref(dims), ctypes.byref(w), None, 0, None, None, None, P,
+                           need, None) == B.MOE_OK
+    assert lib.moe_route(ctypes.byref(dims), ctypes.byref(w), None, 0, None, None, P, need,
+                         None) == B.MOE_OK
+    assert lib.moe_combine(ctypes.byref(dims), ctypes.byref(w), None, 0, None, None, None, None,
+                           None, None, None) == B.MOE_OK

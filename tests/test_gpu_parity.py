@@ -1,0 +1,221 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small variants of the five workloads are checked stage by stage (route,
+dispatch, expert stage, combine) and end to end; the full-size workloads are
+checked end to end in the same launch configuration the benchmark times,
+with routing and dispatch compared for every token and outputs on a sample
+of tokens the oracle evaluates one by one.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_22_amd import binding as B
+from mixture_experts_layer_22_amd import inputs as I
+from oracle import moe_oracle as O
+from tests import compare as C
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def np_of(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=2)
+def full_inputs(name):
+    return I.make_inputs(I.CONFIGS[name])
+
+
+def make_layer(cfg, inp):
+    return B.MoELayer(cfg, inp, DEV)
+
+
+def x_dev(inp):
+    return B.to_device(inp["x"], DEV)
+
+
+# ------------------------------------------------------------ stage by stage
+
+@pytest.mark.parametrize("name", I.CONFIG_ORDER)
+def test_small_stagewise(name):
+    cfg = I.small_variant(name)
+    say("small stagewise", name, cfg.T, cfg.d, cfg.E, cfg.k)
+    inp = I.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    x = x_dev(inp)
+    idx, gate = layer.route(x)
+    torch.cuda.synchronize()
+    idx_np, gate_np = idx.cpu().numpy(), gate.cpu().numpy()
+    C.check_routing(cfg, inp, idx_np, gate_np)
+
+    counts, offsets, perm, inv = layer.dispatch(idx)
+    torch.cuda.synchronize()
+    C.check_dispatch(cfg, idx_np, counts.cpu().numpy(), offsets.cpu().numpy(),
+                     perm.cpu().numpy(), inv.cpu().numpy())
+
+    y, sy = layer.expert_ffn(x, idx, perm, offsets)
+    torch.cuda.synchronize()
+    _, o_off, o_perm, o_inv = O.dispatch(idx_np, cfg.E)
+    tol = C.out_tol(cfg)
+    if cfg.router == I.ROUTER_PRODUCT_KEY:
+        h_ref = O.atomic_h(cfg, inp, idx_np, o_perm)
+        h = y.cpu().numpy()[:h_ref.size]
+        assert np.max(np.abs(h - h_ref)) <= tol * max(1.0, np.max(np.abs(h_ref)))
+    else:
+        Y_ref, SY_ref = O.expert_ffn(cfg, inp, idx_np, o_perm, o_off)
+        if Y_ref.shape[0]:
+            assert C.max_rel_l2(np_of(y[:Y_ref.shape[0]]), Y_ref) <= tol
+        if cfg.n_shared:
+            assert C.max_rel_l2(np_of(sy), SY_ref) <= tol
+
+    out = layer.combine(x, idx, gate, inv, y, sy)
+    out_f = layer.forward(x)
+    torch.cuda.synchronize()
+    ref, _, _ = O.forward(cfg, inp, idx_np, gate_np.astype(np.float64))
+    assert C.max_rel_l2(np_of(out), ref) <= tol
+    assert torch.equal(out, out_f), "forward differs from the staged calls"
+
+
+# ------------------------------------------------------------------ full size
+
+@pytest.mark.parametrize("name", I.CONFIG_ORDER)
+def test_full_size(name):
+    cfg = I.CONFIGS[name]
+    say("full size", name, "T", cfg.T)
+    inp = full_inputs(name)
+    layer = make_layer(cfg, inp)
+    x = x_dev(inp)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
+    out = layer.forward(x, topk_idx=idx, topk_gate=gate)
+    torch.cuda.synchronize()
+    idx_np, gate_np = idx.cpu().numpy(), gate.cpu().numpy()
+    ties = C.check_routing(cfg, inp, idx_np, gate_np)
+    say("  routing ok, near-tie tokens:", ties)
+    counts, offsets, perm, inv = layer.dispatch(idx)
+    torch.cuda.synchronize()
+    C.check_dispatch(cfg, idx_np, counts.cpu().numpy(), offsets.cpu().numpy(),
+                     perm.cpu().numpy(), inv.cpu().numpy())
+    rng = np.random.default_rng(0)
+    n_s = min(cfg.T, 48)
+    tok = np.sort(rng.choice(cfg.T, size=n_s, replace=False))
+    tok[0], tok[-1] = 0, cfg.T - 1
+    tok = np.unique(tok)
+    ref, _, _ = O.forward(cfg, inp, idx_np, gate_np.astype(np.float64), tokens=tok)
+    err = C.max_rel_l2(np_of(out)[tok], ref)
+    say("  sampled output rel-L2", err)
+    assert err <= C.out_tol(cfg)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def _forward_vs_oracle(cfg, inp, tokens=None):
+    layer = make_layer(cfg, inp)
+    x = x_dev(inp)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
+    out = layer.forward(x, topk_idx=idx, topk_gate=gate)
+    torch.cuda.synchronize()
+    idx_np, gate_np = idx.cpu().numpy(), gate.cpu().numpy()
+    C.check_routing(cfg, inp, idx_np, gate_np)
+    ref, _, _ = O.forward(cfg, inp, idx_np, gate_np.astype(np.float64), tokens=tokens)
+    got = np_of(out) if tokens is None else np_of(out)[tokens]
+    assert C.max_rel_l2(got, ref) <= C.out_tol(cfg)
+    return layer, x, out, idx_np
+
+
+@pytest.mark.parametrize("T", [1, 2, 31, 33, 257])
+def test_ragged_T(T):
+    cfg = I.small_variant("deepseek16b").replace(T=T)
+    say("ragged T", T)
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
+def test_T_zero():
+    cfg = I.small_variant("moepp")
+    inp = I.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    x = torch.empty((0, cfg.d), dtype=torch.bfloat16, device=DEV)
+    out = layer.forward(x)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.d)
+
+
+def test_all_tokens_one_expert():
+    """Bias makes expert 3 every token's first choice: one huge group, the
+    rest nearly empty."""
+    cfg = I.small_variant("deepseek16b").replace(T=600, k=2)
+    inp = I.make_inputs(cfg)
+    b = np.zeros(cfg.E, np.float32)
+    b[3] = 50.0
+    inp["router_bias"] = b
+    say("one hot expert")
+    _, _, _, idx_np = _forward_vs_oracle(cfg, inp)
+    assert np.all(idx_np[:, 0] == 3)
+
+
+def test_k_equals_E_and_empty_experts():
+    cfg = I.small_variant("qwen3-decode").replace(E=8, E_ffn=8, k=8, T=40)
+    say("k = E")
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+    # many experts, few tokens: most groups empty
+    cfg = I.small_variant("qwen3-decode").replace(E=200, E_ffn=200, k=2, T=3)
+    say("mostly empty experts")
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
+def test_single_expert():
+    cfg = I.small_variant("deepseek16b").replace(E=1, E_ffn=1, k=1, n_shared=0, T=70,
+                                                 renorm=True, zipf_s=None)
+    say("single expert")
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.1])
+def test_moepp_tau(tau):
+    cfg = I.small_variant("moepp").replace(tau=tau, T=400)
+    say("moe++ tau", tau)
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
+def test_fp32_product_key_and_shared():
+    """fp32 atomic layer, plus the product-key layer with a shared dense
+    SwiGLU branch beside the atomic experts."""
+    cfg = I.small_variant("atomic-pk").replace(dtype=I.DT_F32)
+    say("fp32 product key")
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+    cfg = I.small_variant("atomic-pk").replace(n_shared=1, f_shared=192)
+    say("product key + shared")
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
+def test_fp32_bigger_groups():
+    cfg = I.CONFIGS["tiny-fp32"].replace(T=300, k=3, n_shared=1, f_shared=128, seed=11)
+    say("fp32 bigger")
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
+@pytest.mark.parametrize("name", ["deepseek16b", "atomic-pk", "moepp"])
+def test_deterministic(name):
+    cfg = I.small_variant(name).replace(T=300)
+    inp = I.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    x = x_dev(inp)
+    say("determinism", name)
+    a = layer.forward(x).clone()
+    b = layer.forward(x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

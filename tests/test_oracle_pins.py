@@ -346,12 +346,12 @@ def dense_bruteforce(cfg, inp, idx, gate):
         for j in range(cfg.k):
             G[t, idx[t, j]] += gate[t, j]
     out = np.zeros((T, cfg.d))
-    if cfg.router == I.ROUTER_PRODUCT_KEY:
-        H = F.silu(torch.from_numpy(X) @ torch.from_numpy(f64(inp["atom_u"])).T).numpy()
-        return (G * H) @ f64(inp["atom_w"])
     for s in range(cfg.n_shared):
         out += _torch_swiglu(X, f64(inp["shared_gate"][s]), f64(inp["shared_up"][s]),
                              f64(inp["shared_down"][s]))
+    if cfg.router == I.ROUTER_PRODUCT_KEY:
+        H = F.silu(torch.from_numpy(X) @ torch.from_numpy(f64(inp["atom_u"])).T).numpy()
+        return out + (G * H) @ f64(inp["atom_w"])
     for e in range(cfg.E_ffn):
         Ye = _torch_swiglu(X, f64(inp["w_gate"][e]), f64(inp["w_up"][e]), f64(inp["w_down"][e]))
         out += G[:, e:e + 1] * Ye
@@ -367,9 +367,12 @@ def dense_bruteforce(cfg, inp, idx, gate):
     return out
 
 
-@pytest.mark.parametrize("name", I.CONFIG_ORDER)
+@pytest.mark.parametrize("name", I.CONFIG_ORDER + ["atomic-pk+shared"])
 def test_layer_matches_dense_bruteforce(name):
-    cfg = I.small_variant(name)
+    if name == "atomic-pk+shared":
+        cfg = I.small_variant("atomic-pk").replace(n_shared=1, f_shared=64)
+    else:
+        cfg = I.small_variant(name)
     inp = I.make_inputs(cfg)
     out, idx, gate = O.forward(cfg, inp)
     ref = dense_bruteforce(cfg, inp, idx, gate)
