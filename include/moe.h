@@ -84,7 +84,8 @@ extern "C" {
 typedef void* moe_stream;  /* a hipStream_t */
 
 /* Layer shape and options (host struct).
- *   d        model width; a multiple of 64.
+ *   d        model width; a multiple of 64 (of 128 for the product key,
+ *            whose halves feed the row and column keys).
  *   E        routed experts, including zero-computation ones (product key:
  *            E = pk_rows * pk_cols atomic experts).
  *   E_ffn    SwiGLU experts are ids [0, E_ffn); ids [E_ffn, E) are
@@ -212,6 +213,25 @@ int32_t moe_forward(const moe_dims* dims, const moe_weights* w, const void* x,
                     int64_t T, void* out, int32_t* topk_idx_opt,
                     float* topk_gate_opt, void* ws, size_t ws_bytes,
                     moe_stream stream);
+
+/* Number of phases moe_forward_traced marks with events. */
+#define MOE_N_PHASES 6
+
+/* moe_forward, plus timing marks for profiling the phases of the pass
+ * (route, dispatch, tile list, expert stage 1 = grouped GEMM1 or atomic
+ * activations, expert stage 2 = grouped GEMM2, combine).
+ *   events  NULL, or MOE_N_PHASES + 1 caller-created hipEvent_t handles;
+ *           events[i] is recorded on `stream` just before phase i is
+ *           enqueued and events[MOE_N_PHASES] after the last one, so
+ *           hipEventElapsedTime(events[i], events[i+1]) is phase i's device
+ *           time.  A phase with no work for the layer gets zero width.
+ * Same arguments, results and errors as moe_forward otherwise; a failed
+ * event record returns MOE_ERR_HIP. */
+int32_t moe_forward_traced(const moe_dims* dims, const moe_weights* w,
+                           const void* x, int64_t T, void* out,
+                           int32_t* topk_idx_opt, float* topk_gate_opt,
+                           void* ws, size_t ws_bytes, moe_stream stream,
+                           void* const* events);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,8 @@ import torch
 from . import inputs as _inp
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+# MOE_LIB_PATH selects another build of the same library (profiling builds)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, 1, 2, 3
 MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 4, 5, 6
@@ -26,7 +27,9 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_MAX_ZC = 8
 
 EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route", "moe_dispatch",
-            "moe_expert_ffn", "moe_combine", "moe_forward"]
+            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced"]
+MOE_N_PHASES = 6
+PHASES = ["route", "dispatch", "tiles", "expert1", "expert2", "combine"]
 
 
 class MoeError(RuntimeError):
@@ -84,6 +87,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_combine.argtypes = [dims_p, w_p, P, i64, P, P, P, P, P, P, P]
     lib.moe_forward.restype = ctypes.c_int32
     lib.moe_forward.argtypes = [dims_p, w_p, P, i64, P, P, P, P, sz, P]
+    lib.moe_forward_traced.restype = ctypes.c_int32
+    lib.moe_forward_traced.argtypes = [dims_p, w_p, P, i64, P, P, P, P, sz, P,
+                                       ctypes.POINTER(ctypes.c_void_p)]
     _lib = lib
     return lib
 
@@ -192,6 +198,18 @@ def moe_forward(dims, w: DeviceWeights, x, T, out, ws, topk_idx=None, topk_gate=
     _check(load().moe_forward(ctypes.byref(dims), ctypes.byref(w.struct), _ptr(x), int(T),
                               _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(ws),
                               0 if ws is None else ws.numel(), _stream(stream)), "moe_forward")
+
+
+def moe_forward_traced(dims, w: DeviceWeights, x, T, out, ws, events, topk_idx=None,
+                       topk_gate=None, stream=None):
+    """events: MOE_N_PHASES + 1 torch.cuda.Event(enable_timing=True) objects
+    (torch creates the underlying hipEvent lazily, so record each once
+    before the first call)."""
+    arr = (ctypes.c_void_p * (MOE_N_PHASES + 1))(*[e.cuda_event for e in events])
+    _check(load().moe_forward_traced(ctypes.byref(dims), ctypes.byref(w.struct), _ptr(x),
+                                     int(T), _ptr(out), _ptr(topk_idx), _ptr(topk_gate),
+                                     _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(stream), arr), "moe_forward_traced")
 
 
 # ---------------------------------------------------------------- convenience

@@ -37,7 +37,7 @@ int32_t validate_dims(const moe_dims* d, int64_t T) {
       if (d->zc_kind[z] < MOE_ZC_ZERO || d->zc_kind[z] > MOE_ZC_CONST) return MOE_ERR_SHAPE;
     if (d->E_ffn > 0 && (d->f <= 0 || d->f % 64 != 0)) return MOE_ERR_SHAPE;
   } else if (d->router_kind == MOE_ROUTER_PRODUCT_KEY) {
-    if (d->E_ffn != 0) return MOE_ERR_SHAPE;
+    if (d->E_ffn != 0 || d->d % 128 != 0) return MOE_ERR_SHAPE;
     if (d->pk_rows < 1 || d->pk_cols < 1 || d->pk_rows > MOE_MAX_PK_SIDE ||
         d->pk_cols > MOE_MAX_PK_SIDE)
       return MOE_ERR_SHAPE;
@@ -176,15 +176,20 @@ int32_t do_route(const moe_dims* d, const moe_weights* w, const void* x, int64_t
 
 int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64_t T,
                    const int32_t* idx, const int32_t* perm, const int32_t* offsets, void* y,
-                   void* shared_y, void* ws, const Layout& L, hipStream_t st) {
+                   void* shared_y, void* ws, const Layout& L, hipStream_t st,
+                   void* const* ev = nullptr) {
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+  };
+  const int E_groups = is_pk(d) ? 0 : d->E_ffn;
+  const bool gemms = E_groups > 0 || d->n_shared > 0;
+  int4* tiles = at<int4*>(ws, L.tiles);
+  int32_t* ntiles = at<int32_t*>(ws, L.ntiles);
+  if (gemms) MOE_TRY(launch_build_tiles(offsets, E_groups, d->n_shared, T, L.BM, tiles, ntiles, st));
+  MOE_TRY(mark(3));
   if (is_pk(d)) {
     MOE_TRY(launch_atomic_h(d->dtype, x, w->atom_u, idx, perm, L.n, d->k, d->d, (float*)y, st));
   }
-  const int E_groups = is_pk(d) ? 0 : d->E_ffn;
-  if (E_groups == 0 && d->n_shared == 0) return MOE_OK;
-  int4* tiles = at<int4*>(ws, L.tiles);
-  int32_t* ntiles = at<int32_t*>(ws, L.ntiles);
-  MOE_TRY(launch_build_tiles(offsets, E_groups, d->n_shared, T, L.BM, tiles, ntiles, st));
   void* H = at<void*>(ws, L.h);
   void* Hs = at<void*>(ws, L.hs);
   GemmArgs g1;
@@ -206,7 +211,8 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   g1.N_shared = d->n_shared ? d->f_shared : 0;
   g1.K_routed = d->d;
   g1.K_shared = d->d;
-  MOE_TRY(launch_grouped_gemm(d->dtype, true, L.BM, g1, L.max_tiles, st));
+  if (gemms) MOE_TRY(launch_grouped_gemm(d->dtype, true, L.BM, g1, L.max_tiles, st));
+  MOE_TRY(mark(4));
   GemmArgs g2 = g1;
   g2.a_x = nullptr;
   g2.perm = nullptr;
@@ -222,7 +228,7 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   g2.N_shared = d->n_shared ? d->d : 0;
   g2.K_routed = E_groups ? d->f : 0;
   g2.K_shared = d->n_shared ? d->f_shared : 0;
-  MOE_TRY(launch_grouped_gemm(d->dtype, false, L.BM, g2, L.max_tiles, st));
+  if (gemms) MOE_TRY(launch_grouped_gemm(d->dtype, false, L.BM, g2, L.max_tiles, st));
   return MOE_OK;
 }
 
@@ -353,18 +359,24 @@ int32_t moe_combine(const moe_dims* dims, const moe_weights* w, const void* x, i
                     (hipStream_t)stream);
 }
 
-int32_t moe_forward(const moe_dims* dims, const moe_weights* w, const void* x, int64_t T,
-                    void* out, int32_t* topk_idx_opt, float* topk_gate_opt, void* ws,
-                    size_t ws_bytes, moe_stream stream) {
+int32_t moe_forward_traced(const moe_dims* dims, const moe_weights* w, const void* x,
+                           int64_t T, void* out, int32_t* topk_idx_opt, float* topk_gate_opt,
+                           void* ws, size_t ws_bytes, moe_stream stream, void* const* events) {
   int32_t s = validate_dims(dims, T);
   if (s != MOE_OK) return s;
   if ((s = check_weights(dims, w, true, true, true)) != MOE_OK) return s;
   if (T > 0 && (!x || !out)) return MOE_ERR_NULL;
   if (misaligned(x) || misaligned(out)) return MOE_ERR_SHAPE;
+  if (events)
+    for (int i = 0; i <= MOE_N_PHASES; i++)
+      if (!events[i]) return MOE_ERR_NULL;
   Layout L = make_layout(dims, T);
   if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   hipStream_t st = (hipStream_t)stream;
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
+  };
   int32_t* idx = topk_idx_opt ? topk_idx_opt : at<int32_t*>(ws, L.idx);
   float* gate = topk_gate_opt ? topk_gate_opt : at<float*>(ws, L.gate);
   int32_t* counts = at<int32_t*>(ws, L.counts);
@@ -373,11 +385,25 @@ int32_t moe_forward(const moe_dims* dims, const moe_weights* w, const void* x, i
   int32_t* inv = at<int32_t*>(ws, L.inv);
   void* y = at<void*>(ws, L.y);
   void* sy = dims->n_shared ? at<void*>(ws, L.sy) : nullptr;
+  MOE_TRY(mark(0));
   if ((s = do_route(dims, w, x, T, idx, gate, ws, L, st)) != MOE_OK) return s;
+  MOE_TRY(mark(1));
   MOE_TRY(launch_dispatch(idx, L.n, dims->E, counts, offsets, perm, inv,
                           at<int32_t*>(ws, L.disp), st));
-  if ((s = do_experts(dims, w, x, T, idx, perm, offsets, y, sy, ws, L, st)) != MOE_OK) return s;
-  return do_combine(dims, w, x, T, idx, gate, inv, y, sy, out, st);
+  MOE_TRY(mark(2));
+  if ((s = do_experts(dims, w, x, T, idx, perm, offsets, y, sy, ws, L, st, events)) != MOE_OK)
+    return s;
+  MOE_TRY(mark(5));
+  if ((s = do_combine(dims, w, x, T, idx, gate, inv, y, sy, out, st)) != MOE_OK) return s;
+  MOE_TRY(mark(6));
+  return MOE_OK;
+}
+
+int32_t moe_forward(const moe_dims* dims, const moe_weights* w, const void* x, int64_t T,
+                    void* out, int32_t* topk_idx_opt, float* topk_gate_opt, void* ws,
+                    size_t ws_bytes, moe_stream stream) {
+  return moe_forward_traced(dims, w, x, T, out, topk_idx_opt, topk_gate_opt, ws, ws_bytes,
+                            stream, nullptr);
 }
 
 }  // extern "C"

@@ -66,6 +66,39 @@ __global__ __launch_bounds__(1024) void k_scan_single_block(const int32_t* in, i
   if (write_total && tid == 1023) out[n] = part[1023];
 }
 
+// Single-pass dispatch (E <= 256): exclusive scan of the digit-major tile
+// histogram in place, and from it the expert offsets (the scanned value at
+// (e, tile 0)) and counts.
+__global__ __launch_bounds__(1024) void k_dispatch_scan(int32_t* hist, int64_t len, int nb, int E,
+                                                        int64_t n, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (len + 1023) / 1024;
+  const int64_t lo = tid * per;
+  const int64_t hi = lo + per < len ? lo + per : len;
+  int32_t s = 0;
+  for (int64_t i = lo; i < hi; i++) s += hist[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int32_t v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = tid ? part[tid - 1] : 0;
+  for (int64_t i = lo; i < hi; i++) {
+    int32_t v = hist[i];
+    hist[i] = run;
+    if (i % nb == 0 && i / nb < E) offsets[i / nb] = run;
+    run += v;
+  }
+  if (tid == 0) offsets[E] = (int32_t)n;
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) counts[e] = offsets[e + 1] - offsets[e];
+}
+
 __device__ __forceinline__ int radix_digit(const int32_t* idx, int32_t task, int shift, int mask) {
   return (idx[task] >> shift) & mask;
 }
@@ -96,10 +129,11 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __r
 // Stable scatter.  Items of a tile are taken in task order r*256 + w*64 + l;
 // an item's destination is base[digit, tile] + (same-digit items earlier in
 // the tile).  Same-digit lanes of a wave are found with one ballot per key
-// bit.
+// bit.  The last pass also writes the inverse permutation.
 __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ src, int64_t n, int shift,
-    int bits, const int32_t* __restrict__ hist_scanned, int nb, int32_t* __restrict__ dst) {
+    int bits, const int32_t* __restrict__ hist_scanned, int nb, int32_t* __restrict__ dst,
+    int32_t* __restrict__ inv) {
   __shared__ int32_t run[256];
   __shared__ int32_t wcnt[kRadixThreads / 64][256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -131,6 +165,7 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
       int32_t pos = run[dg] + rank;
       for (int ww = 0; ww < w; ww++) pos += wcnt[ww][dg];
       dst[pos] = task;
+      if (inv) inv[task] = pos;
     }
     __syncthreads();
     int32_t add = 0;
@@ -142,12 +177,6 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     run[tid] += add;
     __syncthreads();
   }
-}
-
-__global__ void k_inverse_perm(const int32_t* __restrict__ perm, int64_t n,
-                               int32_t* __restrict__ inv) {
-  int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (p < n) inv[perm[p]] = (int32_t)p;
 }
 
 // ------------------------------------------------------------------------
@@ -164,26 +193,43 @@ int64_t dispatch_scratch_ints(int64_t n, int E) {
 hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* scratch,
                            hipStream_t st) {
-  // counts and offsets
-  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)cdiv(E, 256)), dim3(256), 0, st, counts, 0,
-                     (int64_t)E);
-  if (n > 0)
-    hipLaunchKernelGGL(k_count_experts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, idx, n,
-                       E, counts);
-  hipLaunchKernelGGL(k_scan_single_block, dim3(1), dim3(1024), 0, st, counts, offsets,
-                     (int64_t)E, 1);
-  if (n == 0) return hipGetLastError();
   int bits = 0;
   while ((1ll << bits) < E) bits++;
   if (bits == 0) bits = 1;  // one expert: a pass on a constant digit keeps task order
   const int nb = (int)cdiv(n, kRadixTile);
   int32_t* hist = scratch;
   int32_t* tmp = scratch + 256 * (int64_t)nb;
+  if (n == 0) {
+    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)cdiv(E, 256)), dim3(256), 0, st, counts, 0,
+                       (int64_t)E);
+    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)cdiv(E + 1, 256)), dim3(256), 0, st, offsets,
+                       0, (int64_t)E + 1);
+    return hipGetLastError();
+  }
+  if (bits <= 8) {
+    // one pass: histogram, scan (+ counts and offsets), stable scatter
+    hipLaunchKernelGGL(k_radix_hist, dim3(nb), dim3(kRadixThreads), 0, st, idx,
+                       (const int32_t*)nullptr, n, 0, bits, hist, nb);
+    hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, st, hist,
+                       (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets);
+    hipLaunchKernelGGL(k_radix_scatter, dim3(nb), dim3(kRadixThreads), 0, st, idx,
+                       (const int32_t*)nullptr, n, 0, bits, hist, nb, perm, inv_perm);
+    return hipGetLastError();
+  }
+  // many experts: per-expert counts by atomics on global counters (spread
+  // over many bins), then 8-bit LSD passes
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)cdiv(E, 256)), dim3(256), 0, st, counts, 0,
+                     (int64_t)E);
+  hipLaunchKernelGGL(k_count_experts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, idx, n, E,
+                     counts);
+  hipLaunchKernelGGL(k_scan_single_block, dim3(1), dim3(1024), 0, st, counts, offsets,
+                     (int64_t)E, 1);
   const int passes = (bits + 7) / 8;
   const int32_t* src = nullptr;
   for (int p = 0; p < passes; p++) {
     const int shift = 8 * p;
     const int pb = bits - shift < 8 ? bits - shift : 8;
+    const bool last = p == passes - 1;
     // ping-pong so that the last pass lands in perm
     int32_t* dst = ((passes - 1 - p) % 2) ? tmp : perm;
     hipLaunchKernelGGL(k_radix_hist, dim3(nb), dim3(kRadixThreads), 0, st, idx, src, n, shift,
@@ -191,11 +237,9 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     hipLaunchKernelGGL(k_scan_single_block, dim3(1), dim3(1024), 0, st, hist, hist,
                        (int64_t)(1 << pb) * nb, 0);
     hipLaunchKernelGGL(k_radix_scatter, dim3(nb), dim3(kRadixThreads), 0, st, idx, src, n, shift,
-                       pb, hist, nb, dst);
+                       pb, hist, nb, dst, last ? inv_perm : (int32_t*)nullptr);
     src = dst;
   }
-  hipLaunchKernelGGL(k_inverse_perm, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, perm, n,
-                     inv_perm);
   return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@
 // the B tile holds BN/2 W_gate rows and the same BN/2 W_up rows, and each
 // wave's fragments pair gate and up columns, so silu(g)*u is formed in
 // registers and H is written once, in bf16.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -83,6 +85,25 @@ __device__ __forceinline__ T* c_row(const GemmArgs& a, const TileCtx<SWIGLU>& c,
 }
 
 // ------------------------------------------------------------------------
+// Block -> (M tile, N tile).  Workgroups are handed to the 8 XCDs round-robin
+// (block b runs on XCD b % 8), and each XCD has its own L2.  The W =
+// ntiles * n_ntiles work items are listed M-tile major (the N tiles of one
+// M tile are consecutive: they share the gathered A rows; consecutive M tiles
+// of one expert share its weights) and cut into 8 contiguous chunks, chunk x
+// going to the blocks of XCD x in order.  Blocks past the real work exit.
+__device__ __forceinline__ bool work_item(int ntiles, int n_ntiles, int& m_tile, int& n_tile) {
+  const int W = ntiles * n_ntiles;
+  const int b = blockIdx.x;
+  const int chunk = (W + 7) / 8;
+  const int slot = b / 8;
+  const int w = (b % 8) * chunk + slot;
+  if (slot >= chunk || w >= W) return false;
+  m_tile = w / n_ntiles;
+  n_tile = w - m_tile * n_ntiles;
+  return true;
+}
+
+// ------------------------------------------------------------------------
 // bf16 MFMA grouped GEMM.  WM x WN waves, each FM x FN 32x32 fragments.
 template <int WM, int WN, int FM, int FN, bool SWIGLU>
 __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs args) {
@@ -99,11 +120,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * BK];
 
-  const int tile_id = blockIdx.x;
-  if (tile_id >= *args.ntiles) return;
+  int tile_id, n_tile;
+  if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
   const int4 tl = args.tiles[tile_id];
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl);
-  const int n0 = blockIdx.y * BNO;
+  const int n0 = n_tile * BNO;
   if (n0 >= c.N) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -217,13 +238,207 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
 }
 
 // ------------------------------------------------------------------------
+// bf16 MFMA grouped GEMM, 256 x 256 (B rows) tiles, direct-to-LDS pipeline.
+//
+// Global -> LDS copies use global_load_lds_dwordx4 (no staging registers):
+// lane i of a wave lands 16 bytes at LDS base + 16 i.  K is cut into 32-wide
+// tiles; four LDS stages of 32 KB (A 256 x 32 + B 256 x 32 bf16) keep three
+// tiles in flight while the fourth is multiplied, so HBM/L2 latency hides
+// behind about 3000 cycles of MFMA work.  One barrier per K tile.
+//
+// LDS rows are 64 bytes (4 chunks of 16 B); chunk c of row r sits at
+// c ^ f(r), f(r) = ((r >> 1) & 3) ^ ((r >> 2) & 3).  An MFMA fragment read
+// (32 consecutive rows, one chunk) then touches distinct banks within every
+// 8 lanes (32 x 4-byte banks) and within every 16 lanes (64 banks).
+//
+// Rows past the group's end (A) or past N (B) are pointed at a valid row:
+// their products only reach output rows / columns that are not stored.
+__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+__device__ __forceinline__ void dl_copy16(const uint16_t* g, uint16_t* l) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their max)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
+  constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;
+  constexpr int FM = 4, FN = 4;                // 32x32 fragments per wave (2 x 2 waves)
+  constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 16384 bf16 = 32 KB
+  constexpr int LOADS = 8;                     // 1 KB copies per wave per K tile
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE_ELEMS];
+
+  int tile_id, n_tile;
+  if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
+  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
+  const int n0 = n_tile * BNO;
+  if (n0 >= c.N) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // loader: copy j (0..7) of this wave covers tile rows (wave*4 + j%4)*16 +
+  // lane/4 of A (j < 4) or B (j >= 4); the lane's 16 B is logical chunk
+  // (lane & 3) ^ f(row) of that row.
+  const uint16_t* src[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; j++) {
+    const int row = (wave * 4 + (j & 3)) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ lds_swz(row);
+    const uint16_t* p;
+    if (j < 4) {
+      p = a_row<uint16_t, SWIGLU>(args, c, row);
+      if (!p) p = a_row<uint16_t, SWIGLU>(args, c, 0);
+    } else {
+      p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, row);
+      if (!p) p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, SWIGLU && row >= BN / 2 ? BN / 2 : 0);
+    }
+    src[j] = p + chunk * 8;
+  }
+  auto issue = [&](int kt) {
+    uint16_t* st = lds + (kt % STAGES) * STAGE_ELEMS;
+    const int col = kt * BK;
+#pragma unroll
+    for (int j = 0; j < LOADS; j++) {
+      const int row0 = (j < 4 ? 0 : BM) + (wave * 4 + (j & 3)) * 16;
+      dl_copy16(src[j] + col, st + row0 * BK);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++) acc[i][j] = f32x16{};
+
+  int brow[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; fn++) {
+    if (SWIGLU) {
+      brow[fn] = (fn < 2) ? (wn * 2 + fn) * 32 : BN / 2 + (wn * 2 + fn - 2) * 32;
+    } else {
+      brow[fn] = (wn * FN + fn) * 32;
+    }
+  }
+  const int frow = lane & 31;
+  const int fsw = lds_swz(frow);
+  const int fhalf = lane >> 5;
+
+  const int nk = c.K / BK;
+  // fragments of one K tile (two 16-wide MFMA steps), double buffered in
+  // registers: tile kt+1 is read from LDS while tile kt is multiplied
+  bf16x8 fa[2][2][FM], fb[2][2][FN];
+  auto read_frags = [&](int kt, int buf) {
+    const uint16_t* st = lds + (kt % STAGES) * STAGE_ELEMS;
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      const int ch = ((2 * s + fhalf) ^ fsw) * 8;
+#pragma unroll
+      for (int fm = 0; fm < FM; fm++)
+        fa[buf][s][fm] = *reinterpret_cast<const bf16x8*>(st + ((wm * FM + fm) * 32 + frow) * BK + ch);
+#pragma unroll
+      for (int fn = 0; fn < FN; fn++)
+        fb[buf][s][fn] = *reinterpret_cast<const bf16x8*>(st + (BM + brow[fn] + frow) * BK + ch);
+    }
+  };
+  auto mfma_tile = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][s][fm], fb[buf][s][fn],
+                                                                acc[fm][fn], 0, 0, 0);
+  };
+  // wait until this wave's copies of tile t have landed: at most the copies
+  // of the tiles issued after it (up to STAGES-1 of them) may be in flight
+  auto wait_tile = [&](int t, int issued_upto) {
+    const int later = (issued_upto < nk - 1 ? issued_upto : nk - 1) - t;
+    if (later >= 3) wait_vmcnt<3 * LOADS>();
+    else if (later == 2) wait_vmcnt<2 * LOADS>();
+    else if (later == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+  };
+
+  // prologue: fill all stages, then stage tile 0's fragments
+#pragma unroll
+  for (int t = 0; t < STAGES; t++)
+    if (t < nk) issue(t);
+  wait_tile(0, STAGES - 1);
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, 0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+
+  // one K tile: make tile kt+1 visible, refill tile kt's stage, read tile
+  // kt+1's fragments into the other register buffer, multiply tile kt
+  auto step = [&](int kt, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    if (kt + 1 < nk) {
+      // tile kt+1 has landed for every wave, and every wave has finished
+      // reading tile kt from LDS (its reads completed before this barrier),
+      // so tile kt's stage can be refilled with tile kt+STAGES
+      wait_tile(kt + 1, kt + STAGES - 1);
+      __builtin_amdgcn_s_barrier();
+      if (kt + STAGES < nk) issue(kt + STAGES);
+      read_frags(kt + 1, buf ^ 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_tile(buf);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): next tile's fragments are in registers
+  };
+  // nk is even (K is a multiple of 64): unrolled by two so the register
+  // buffer index is a compile-time constant
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+  }
+
+  const int ccol = lane & 31;
+#pragma unroll
+  for (int fm = 0; fm < FM; fm++) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int row = (wm * FM + fm) * 32 + 8 * (j >> 2) + 4 * fhalf + (j & 3);
+      if (row >= c.nr) continue;
+      uint16_t* out = c_row<uint16_t, SWIGLU>(args, c, row);
+      if (SWIGLU) {
+#pragma unroll
+        for (int fn = 0; fn < 2; fn++) {
+          const int col = n0 + (wn * 2 + fn) * 32 + ccol;
+          const float g = acc[fm][fn][j], u = acc[fm][fn + 2][j];
+          if (col < c.N) out[col] = f32_to_bf16(silu_f32(g) * u);
+        }
+      } else {
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+          const int col = n0 + (wn * FN + fn) * 32 + ccol;
+          if (col < c.N) out[col] = f32_to_bf16(acc[fm][fn][j]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
 // fp32 layers: plain FMA, one thread per output element, 32-row tiles.
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
-  const int tile_id = blockIdx.x;
-  if (tile_id >= *args.ntiles) return;
+  int tile_id, n_tile;
+  if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
-  const int n0 = blockIdx.y * 64;
+  const int n0 = n_tile * 64;
   if (n0 >= c.N) return;
   const int i = threadIdx.x >> 3;  // local row 0..31
   if (i >= c.nr) return;
@@ -309,34 +524,34 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E_ffn,
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a,
+hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a_in,
                                int64_t max_tiles, hipStream_t st) {
+  GemmArgs a = a_in;
   const int Nmax = a.N_routed > a.N_shared ? a.N_routed : a.N_shared;
   if (max_tiles == 0 || Nmax == 0) return hipSuccess;
+  int bno;
+  if (dtype == MOE_F32) bno = 64;
+  else bno = swiglu ? 128 : 256;  // BN = 256 B rows per tile
+  a.n_ntiles = (int)cdiv(Nmax, bno);
+  // one block per work item, padded so every XCD chunk is covered
+  const unsigned grid = (unsigned)(max_tiles * a.n_ntiles + 8);
   if (dtype == MOE_F32) {
-    dim3 grid((unsigned)max_tiles, (unsigned)cdiv(Nmax, 64));
     if (swiglu)
-      hipLaunchKernelGGL(k_grouped_gemm_f32<true>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3(grid), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL(k_grouped_gemm_f32<false>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(k_grouped_gemm_f32<false>, dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (BM == 256) {
-    constexpr int BN = 256;
-    const int bno = swiglu ? BN / 2 : BN;
-    dim3 grid((unsigned)max_tiles, (unsigned)cdiv(Nmax, bno));
     if (swiglu)
-      hipLaunchKernelGGL((k_grouped_gemm_bf16<2, 2, 4, 4, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_dl<true>), dim3(grid), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((k_grouped_gemm_bf16<2, 2, 4, 4, false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_dl<false>), dim3(grid), dim3(256), 0, st, a);
   } else {
-    constexpr int BN = 256;
-    const int bno = swiglu ? BN / 2 : BN;
-    dim3 grid((unsigned)max_tiles, (unsigned)cdiv(Nmax, bno));
     if (swiglu)
-      hipLaunchKernelGGL((k_grouped_gemm_bf16<1, 4, 1, 2, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_grouped_gemm_bf16<1, 4, 1, 2, true>), dim3(grid), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((k_grouped_gemm_bf16<1, 4, 1, 2, false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_grouped_gemm_bf16<1, 4, 1, 2, false>), dim3(grid), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -26,6 +26,7 @@ struct GemmArgs {
   void* c_shared;
   int N_routed, N_shared;  // output columns
   int K_routed, K_shared;
+  int n_ntiles;            // N tiles per M tile (set by the launcher)
 };
 
 struct CombineArgs {

@@ -35,49 +35,58 @@ __global__ void k_split_router(const float* __restrict__ W, uint16_t* __restrict
 // ------------------------------------------------------------------------
 // logits[t, col_off + n] = x[t, x_off : x_off+K] . W[n, :K]   (n < NL)
 // bf16 x, W given as the three bf16 slices W3[p * slice + n * K + kk].
-// Block: 4 waves in a 2x2 grid, each wave one 32x32 MFMA tile; grid
-// (ceil(T/64), ceil(NL/64)).  Operands go straight from global memory to
-// MFMA registers: per 32-wide K block, lane (r = l%32, q = l/32) loads 16
-// consecutive elements of its row at q*16, and MFMA step s uses elements
-// [q*16 + 8s, +8).  A and B use the same K permutation, so the dot products
-// are unchanged while every row is read as one 64-byte run.
+// Block: 16 tokens x 64 logits, 4 waves of 16x16 (v_mfma_f32_16x16x32_bf16);
+// grid (ceil(T/16), ceil(NL/64)).  Operands go straight from global memory
+// to MFMA registers: per 64-wide K block, lane (r = l%16, q = l/16) loads 16
+// consecutive elements of its row at q*16 and MFMA step s uses elements
+// [q*16 + 8s, +8).  A and B share that K permutation, so the dot products
+// are unchanged while every row is read as one 128-byte run.  The three
+// weight slices accumulate into one fp32 accumulator.
 __global__ __launch_bounds__(256) void k_router_logits_bf16(
     const uint16_t* __restrict__ x, int64_t T, int ldx, int x_off,
     const uint16_t* __restrict__ W3, int64_t slice, int NL, int K,
     float* __restrict__ logits, int ldl, int col_off) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 64 + (wave >> 1) * 32;
-  const int n0 = blockIdx.y * 64 + (wave & 1) * 32;
-  const int r = lane & 31, q = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int n0 = blockIdx.y * 64 + wave * 16;
+  if (n0 >= NL) return;
+  const int r = lane & 15, q = lane >> 4;
   const int64_t am = m0 + r;
   const int bn = n0 + r;
   const bool a_ok = am < T, b_ok = bn < NL;
   const uint16_t* ap = x + (a_ok ? am : 0) * (int64_t)ldx + x_off + q * 16;
   const uint16_t* bp = W3 + (int64_t)(b_ok ? bn : 0) * K + q * 16;
-  f32x16 acc = {};
-  for (int kb = 0; kb < K; kb += 32) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int kb = 0; kb < K; kb += 64) {
     u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
     if (a_ok) {
       a0 = *reinterpret_cast<const u32x4*>(ap + kb);
       a1 = *reinterpret_cast<const u32x4*>(ap + kb + 8);
     }
+    u32x4 b0[3], b1[3];
 #pragma unroll
     for (int p = 0; p < 3; p++) {
-      u32x4 b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+      b0[p] = u32x4{0, 0, 0, 0};
+      b1[p] = u32x4{0, 0, 0, 0};
       if (b_ok) {
-        b0 = *reinterpret_cast<const u32x4*>(bp + p * slice + kb);
-        b1 = *reinterpret_cast<const u32x4*>(bp + p * slice + kb + 8);
+        b0[p] = *reinterpret_cast<const u32x4*>(bp + p * slice + kb);
+        b1[p] = *reinterpret_cast<const u32x4*>(bp + p * slice + kb + 8);
       }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
-                                                    __builtin_bit_cast(bf16x8, b0), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1),
-                                                    __builtin_bit_cast(bf16x8, b1), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; p++) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                    __builtin_bit_cast(bf16x8, b0[p]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                    __builtin_bit_cast(bf16x8, b1[p]), acc, 0, 0, 0);
     }
   }
+  // lane holds C[4 q + j][r]
   const int n = n0 + r;
 #pragma unroll
-  for (int j = 0; j < 16; j++) {
-    int64_t m = m0 + 8 * (j >> 2) + 4 * q + (j & 3);
+  for (int j = 0; j < 4; j++) {
+    const int64_t m = m0 + 4 * q + j;
     if (m < T && n < NL) logits[m * ldl + col_off + n] = acc[j];
   }
 }
@@ -270,7 +279,7 @@ hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, in
                                 int ldl, int col_off, hipStream_t st) {
   if (T == 0 || NL == 0) return hipSuccess;
   if (dtype == MOE_BF16) {
-    dim3 grid((unsigned)cdiv(T, 64), (unsigned)cdiv(NL, 64));
+    dim3 grid((unsigned)cdiv(T, 16), (unsigned)cdiv(NL, 64));
     hipLaunchKernelGGL(k_router_logits_bf16, grid, dim3(256), 0, st, (const uint16_t*)x, T, ldx,
                        x_off, (const uint16_t*)W, slice, NL, K, logits, ldl, col_off);
   } else {
