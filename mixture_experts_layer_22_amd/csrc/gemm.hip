@@ -305,16 +305,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
     }
     src[j] = p + chunk * 8;
   }
-  auto issue = [&](int kt) {
+  auto copy_one = [&](int kt, int j) {
     uint16_t* st = lds + (kt % STAGES) * STAGE_ELEMS;
-    const int col = kt * BK;
-#pragma unroll
-    for (int j = 0; j < LOADS; j++) {
-      const int row0 = (j < 4 ? 0 : BM) + (wave * 4 + (j & 3)) * 16;
-      dl_copy16(src[j] + col, st + row0 * BK);
-    }
+    const int row0 = (j < 4 ? 0 : BM) + (wave * 4 + (j & 3)) * 16;
+    dl_copy16(src[j] + kt * BK, st + row0 * BK);
   };
 
+  // Accumulators hold C^T fragments: the weight fragment is the MFMA's first
+  // operand, so lane l ends up with 4 consecutive output columns of one
+  // output row per 4-element group (stored as one 8-byte write).
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; i++)
@@ -333,36 +332,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
   const int frow = lane & 31;
   const int fsw = lds_swz(frow);
   const int fhalf = lane >> 5;
-
   const int nk = c.K / BK;
+
   // fragments of one K tile (two 16-wide MFMA steps), double buffered in
-  // registers: tile kt+1 is read from LDS while tile kt is multiplied
-  bf16x8 fa[2][2][FM], fb[2][2][FN];
-  auto read_frags = [&](int kt, int buf) {
+  // registers: tile kt+1 is read from LDS while tile kt is multiplied.
+  // Fragment q (0..15) of a tile: step q / 8, then A rows (q%8 < 4) or B rows.
+  bf16x8 fr[2][16];
+  auto read_frag = [&](int kt, int buf, int q) {
     const uint16_t* st = lds + (kt % STAGES) * STAGE_ELEMS;
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-      const int ch = ((2 * s + fhalf) ^ fsw) * 8;
-#pragma unroll
-      for (int fm = 0; fm < FM; fm++)
-        fa[buf][s][fm] = *reinterpret_cast<const bf16x8*>(st + ((wm * FM + fm) * 32 + frow) * BK + ch);
-#pragma unroll
-      for (int fn = 0; fn < FN; fn++)
-        fb[buf][s][fn] = *reinterpret_cast<const bf16x8*>(st + (BM + brow[fn] + frow) * BK + ch);
-    }
+    const int s = q >> 3, i = q & 7;
+    const int ch = ((2 * s + fhalf) ^ fsw) * 8;
+    const int row = i < 4 ? (wm * FM + i) * 32 + frow : BM + brow[i - 4] + frow;
+    fr[buf][q] = *reinterpret_cast<const bf16x8*>(st + row * BK + ch);
   };
-  auto mfma_tile = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < 2; s++)
-#pragma unroll
-      for (int fm = 0; fm < FM; fm++)
-#pragma unroll
-        for (int fn = 0; fn < FN; fn++)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][s][fm], fb[buf][s][fn],
-                                                                acc[fm][fn], 0, 0, 0);
-  };
-  // wait until this wave's copies of tile t have landed: at most the copies
-  // of the tiles issued after it (up to STAGES-1 of them) may be in flight
   auto wait_tile = [&](int t, int issued_upto) {
     const int later = (issued_upto < nk - 1 ? issued_upto : nk - 1) - t;
     if (later >= 3) wait_vmcnt<3 * LOADS>();
@@ -374,59 +356,109 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
   // prologue: fill all stages, then stage tile 0's fragments
 #pragma unroll
   for (int t = 0; t < STAGES; t++)
-    if (t < nk) issue(t);
+    if (t < nk)
+#pragma unroll
+      for (int j = 0; j < LOADS; j++) copy_one(t, j);
   wait_tile(0, STAGES - 1);
   __builtin_amdgcn_s_barrier();
-  read_frags(0, 0);
+#pragma unroll
+  for (int q = 0; q < 16; q++) read_frag(0, 0, q);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
-  // one K tile: make tile kt+1 visible, refill tile kt's stage, read tile
-  // kt+1's fragments into the other register buffer, multiply tile kt
-  auto step = [&](int kt, auto buf_c) {
+  // One K tile: make tile kt+1 visible, then 8 groups of {one copy of tile
+  // kt+STAGES into tile kt's stage, two fragment reads of tile kt+1, four
+  // MFMAs of tile kt}, so the copy issue and LDS reads are spread over the
+  // MFMA stream.
+  auto step = [&](int kt, auto buf_c, auto steady_c) {
     constexpr int buf = decltype(buf_c)::value;
-    if (kt + 1 < nk) {
+    constexpr bool steady = decltype(steady_c)::value;  // copies and reads all valid
+    const bool more = steady || kt + 1 < nk;
+    const bool refill = steady || kt + STAGES < nk;
+    if (more) {
       // tile kt+1 has landed for every wave, and every wave has finished
-      // reading tile kt from LDS (its reads completed before this barrier),
-      // so tile kt's stage can be refilled with tile kt+STAGES
-      wait_tile(kt + 1, kt + STAGES - 1);
+      // reading tile kt from LDS (its reads completed before this barrier)
+      if (steady) wait_vmcnt<2 * LOADS>();
+      else wait_tile(kt + 1, kt + STAGES - 1);
       __builtin_amdgcn_s_barrier();
-      if (kt + STAGES < nk) issue(kt + STAGES);
-      read_frags(kt + 1, buf ^ 1);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_tile(buf);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 8; g++) {
+      if (refill) copy_one(kt + STAGES, g);
+      if (more) {
+        read_frag(kt + 1, buf ^ 1, 2 * g);
+        read_frag(kt + 1, buf ^ 1, 2 * g + 1);
+      }
+      // MFMAs 4g .. 4g+3 of this tile: step s = g / 4, A fragment fm = g % 4
+      const int s = g >> 2, fm = g & 3;
+#pragma unroll
+      for (int fn = 0; fn < FN; fn++)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][8 * s + 4 + fn],
+                                                              fr[buf][8 * s + fm], acc[fm][fn],
+                                                              0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): next tile's fragments are in registers
   };
   // nk is even (K is a multiple of 64): unrolled by two so the register
-  // buffer index is a compile-time constant
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
+  // buffer index is a compile-time constant.  The steady part (every tile
+  // still has a refill) runs without per-group conditions.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using Steady = std::true_type;
+  using Tail = std::false_type;
+  int kt = 0;
+  for (; kt + STAGES < nk; kt += 2) {
+    step(kt, I0{}, Steady{});
+    step(kt + 1, I1{}, Steady{});
+  }
+  for (; kt < nk; kt += 2) {
+    step(kt, I0{}, Tail{});
+    step(kt + 1, I1{}, Tail{});
   }
 
-  const int ccol = lane & 31;
+  // epilogue.  acc[fm][fn][j] = C[row = (wm*FM + fm)*32 + lane%32]
+  //                              [col = fn*32 + 8(j/4) + 4(lane/32) + j%4]
+  // (col relative to the wave's first column).  Full tiles skip the bounds
+  // checks; every store writes 4 consecutive bf16 columns.
+  const bool full_rows = c.nr >= BM;
+  const bool full_cols = n0 + BNO <= c.N;
 #pragma unroll
   for (int fm = 0; fm < FM; fm++) {
+    const int row = (wm * FM + fm) * 32 + frow;
+    if (!full_rows && row >= c.nr) continue;
+    uint16_t* out = c_row<uint16_t, SWIGLU>(args, c, row);
+    if (SWIGLU) {
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int row = (wm * FM + fm) * 32 + 8 * (j >> 2) + 4 * fhalf + (j & 3);
-      if (row >= c.nr) continue;
-      uint16_t* out = c_row<uint16_t, SWIGLU>(args, c, row);
-      if (SWIGLU) {
+      for (int fn = 0; fn < 2; fn++)
 #pragma unroll
-        for (int fn = 0; fn < 2; fn++) {
-          const int col = n0 + (wn * 2 + fn) * 32 + ccol;
-          const float g = acc[fm][fn][j], u = acc[fm][fn + 2][j];
-          if (col < c.N) out[col] = f32_to_bf16(silu_f32(g) * u);
+        for (int g = 0; g < 4; g++) {
+          const int col = n0 + (wn * 2 + fn) * 32 + 8 * g + 4 * fhalf;
+          float h[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const float gt = acc[fm][fn][4 * g + e], up = acc[fm][fn + 2][4 * g + e];
+            h[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          }
+          if (full_cols || col < c.N) {
+            uint2 v;
+            v.x = pack_bf16x2(h[0], h[1]);
+            v.y = pack_bf16x2(h[2], h[3]);
+            *reinterpret_cast<uint2*>(out + col) = v;
+          }
         }
-      } else {
+    } else {
 #pragma unroll
-        for (int fn = 0; fn < FN; fn++) {
-          const int col = n0 + (wn * FN + fn) * 32 + ccol;
-          if (col < c.N) out[col] = f32_to_bf16(acc[fm][fn][j]);
+      for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const int col = n0 + (wn * FN + fn) * 32 + 8 * g + 4 * fhalf;
+          if (full_cols || col < c.N) {
+            uint2 v;
+            v.x = pack_bf16x2(acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1]);
+            v.y = pack_bf16x2(acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]);
+            *reinterpret_cast<uint2*>(out + col) = v;
+          }
         }
-      }
     }
   }
 }
