@@ -64,7 +64,7 @@ bool misaligned(const void* p) { return p && ((uintptr_t)p % 16) != 0; }
 // Workspace layout (one figure for every entry point).
 struct Layout {
   int64_t T, n;
-  int NL, Kw, BM;
+  int NL, Kw, BM, splits;
   int64_t max_tiles;
   size_t w3, logits, disp, tiles, ntiles, h, hs, idx, gate, counts, offsets, perm, inv, y, sy;
   size_t total;
@@ -82,6 +82,7 @@ Layout make_layout(const moe_dims* d, int64_t T) {
     L.NL = d->E;
     L.Kw = d->d;
   }
+  L.splits = router_splits(d->dtype, T, is_pk(d) ? (d->pk_rows > d->pk_cols ? d->pk_rows : d->pk_cols) : d->E, L.Kw);
   L.BM = gemm_tile_rows(d->dtype, L.n, d->E_ffn);
   const int E_groups = is_pk(d) ? 0 : d->E_ffn;
   L.max_tiles = gemm_max_tiles(T, is_pk(d) ? 0 : d->k, E_groups, d->n_shared, L.BM);
@@ -92,7 +93,7 @@ Layout make_layout(const moe_dims* d, int64_t T) {
     return o;
   };
   L.w3 = take(d->dtype == MOE_BF16 ? (size_t)3 * L.NL * L.Kw * 2 : 0);
-  L.logits = take((size_t)T * L.NL * 4);
+  L.logits = take((size_t)L.splits * T * L.NL * 4);
   L.disp = take((size_t)dispatch_scratch_ints(L.n, d->E) * 4);
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
   L.ntiles = take(4);
@@ -154,22 +155,21 @@ int32_t do_route(const moe_dims* d, const moe_weights* w, const void* x, int64_t
     W = w3;
   }
   const int64_t slice = (int64_t)L.NL * L.Kw;
-  const int es = elt_size(d->dtype);
   if (!is_pk(d)) {
     MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, slice, d->E, d->d, logits, d->E, 0,
-                                 st));
-    MOE_TRY(launch_select_topk(logits, T, d->E, d->E_ffn, d->k, d->ffn_logit_scale,
+                                 L.splits, st));
+    MOE_TRY(launch_select_topk(logits, L.splits, T, d->E, d->E_ffn, d->k, d->ffn_logit_scale,
                                w->router_bias, d->renorm, idx, gate, st));
   } else {
     const int K = L.Kw;
-    const void* Wc = reinterpret_cast<const char*>(W) + (size_t)d->pk_rows * K * (d->dtype == MOE_BF16 ? 2 : 4);
-    (void)es;
+    const void* Wc = reinterpret_cast<const char*>(W) +
+                     (size_t)d->pk_rows * K * (d->dtype == MOE_BF16 ? 2 : 4);
     MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, slice, d->pk_rows, K, logits, L.NL,
-                                 0, st));
+                                 0, L.splits, st));
     MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, K, Wc, slice, d->pk_cols, K, logits, L.NL,
-                                 d->pk_rows, st));
-    MOE_TRY(launch_select_pk(logits, T, d->pk_rows, d->pk_cols, d->pk_k_row, d->pk_k_col, d->k,
-                             idx, gate, st));
+                                 d->pk_rows, L.splits, st));
+    MOE_TRY(launch_select_pk(logits, L.splits, T, d->pk_rows, d->pk_cols, d->pk_k_row,
+                             d->pk_k_col, d->k, idx, gate, st));
   }
   return MOE_OK;
 }

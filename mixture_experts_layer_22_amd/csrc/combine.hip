@@ -19,19 +19,54 @@
 namespace moe {
 
 // ------------------------------------------------------------------------
+// 8 layer-dtype elements kept packed in registers until they are used.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ float operator[](int i) const {
+    return (i & 1) ? hi_bf16(w[i >> 1]) : lo_bf16(w[i >> 1]);
+  }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+
+__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// ------------------------------------------------------------------------
 // One wave per token; lane owns 8-element units u = lane + 64 i (i < U).
+// The k slots' (expert, gate, sorted position) are fetched one slot per
+// lane, then expert rows are loaded CH slots at a time so that several row
+// loads are in flight before any is consumed.
 template <typename T, int U>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  constexpr int CH = U >= 4 ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  const int d = a.d, nu = d / 8;
+  const int d = a.d, nu = d / 8, k = a.k;
   float acc[U][8];
 #pragma unroll
   for (int i = 0; i < U; i++)
 #pragma unroll
     for (int q = 0; q < 8; q++) acc[i][q] = 0.f;
 
+  int me = 0, mp = 0;
+  float mg = 0.f;
+  if (lane < k) {
+    me = a.idx[t * k + lane];
+    mg = a.gate[t * k + lane];
+    mp = a.inv_perm[t * k + lane];
+  }
   const T* sy = reinterpret_cast<const T*>(a.shared_y);
   for (int s = 0; s < a.n_shared; s++) {
     const T* row = sy + ((int64_t)s * a.T + t) * d;
@@ -39,84 +74,99 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     for (int i = 0; i < U; i++) {
       const int u = lane + 64 * i;
       if (u < nu) {
-        float v[8];
-        Elt<T>::load8(row + u * 8, v);
+        Raw8<T> r;
+        r.load(row + u * 8);
 #pragma unroll
-        for (int q = 0; q < 8; q++) acc[i][q] += v[q];
+        for (int q = 0; q < 8; q++) acc[i][q] += r[q];
       }
     }
   }
   const T* xrow = reinterpret_cast<const T*>(a.x) + t * d;
   const T* y = reinterpret_cast<const T*>(a.y);
-  for (int j = 0; j < a.k; j++) {
-    const int64_t task = t * a.k + j;
-    const int e = a.idx[task];
-    const float g = a.gate[task];
-    if (e < a.E_ffn) {
-      const T* row = y + (int64_t)a.inv_perm[task] * d;
+  for (int j0 = 0; j0 < k; j0 += CH) {
+    Raw8<T> r[CH][U];
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+      const int j = j0 + c;
+      if (j < k) {
+        const int e = readlane_i(me, j);
+        if (e < a.E_ffn) {
+          const T* row = y + (int64_t)readlane_i(mp, j) * d;
+#pragma unroll
+          for (int i = 0; i < U; i++) {
+            const int u = lane + 64 * i;
+            if (u < nu) r[c][i].load(row + u * 8);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+      const int j = j0 + c;
+      if (j >= k) break;
+      const int e = readlane_i(me, j);
+      const float g = readlane_f(mg, j);
+      if (e < a.E_ffn) {
+#pragma unroll
+        for (int i = 0; i < U; i++)
+          if (lane + 64 * i < nu)
+#pragma unroll
+            for (int q = 0; q < 8; q++) acc[i][q] += g * r[c][i][q];
+        continue;
+      }
+      const int z = e - a.E_ffn;
+      const int kind = a.zc_kind[z];
+      if (kind == MOE_ZC_ZERO) continue;
+      if (kind == MOE_ZC_COPY) {
+#pragma unroll
+        for (int i = 0; i < U; i++) {
+          const int u = lane + 64 * i;
+          if (u < nu) {
+            Raw8<T> xv;
+            xv.load(xrow + u * 8);
+#pragma unroll
+            for (int q = 0; q < 8; q++) acc[i][q] += g * xv[q];
+          }
+        }
+        continue;
+      }
+      // constant expert: [a, b] = softmax(W_c x) over the whole row
+      const int ci = a.const_index[z];
+      const float* wc0 = a.const_wc + (int64_t)ci * 2 * d;
+      const float* wc1 = wc0 + d;
+      const T* vrow = reinterpret_cast<const T*>(a.const_v) + (int64_t)ci * d;
+      float pa = 0.f, pb = 0.f;
 #pragma unroll
       for (int i = 0; i < U; i++) {
         const int u = lane + 64 * i;
         if (u < nu) {
-          float v[8];
-          Elt<T>::load8(row + u * 8, v);
+          Raw8<T> xv;
+          xv.load(xrow + u * 8);
+          float w0[8], w1[8];
+          Elt<float>::load8(wc0 + u * 8, w0);
+          Elt<float>::load8(wc1 + u * 8, w1);
 #pragma unroll
-          for (int q = 0; q < 8; q++) acc[i][q] += g * v[q];
+          for (int q = 0; q < 8; q++) {
+            pa = fmaf(w0[q], xv[q], pa);
+            pb = fmaf(w1[q], xv[q], pb);
+          }
         }
       }
-      continue;
-    }
-    const int z = e - a.E_ffn;
-    const int kind = a.zc_kind[z];
-    if (kind == MOE_ZC_ZERO) continue;
-    if (kind == MOE_ZC_COPY) {
+      pa = wave_sum(pa);
+      pb = wave_sum(pb);
+      const float mx = fmaxf(pa, pb);
+      const float ea = __expf(pa - mx), eb = __expf(pb - mx);
+      const float ca = g * (ea / (ea + eb)), cb = g * (eb / (ea + eb));
 #pragma unroll
       for (int i = 0; i < U; i++) {
         const int u = lane + 64 * i;
         if (u < nu) {
-          float v[8];
-          Elt<T>::load8(xrow + u * 8, v);
+          Raw8<T> xv, vv;
+          xv.load(xrow + u * 8);
+          vv.load(vrow + u * 8);
 #pragma unroll
-          for (int q = 0; q < 8; q++) acc[i][q] += g * v[q];
+          for (int q = 0; q < 8; q++) acc[i][q] += ca * xv[q] + cb * vv[q];
         }
-      }
-      continue;
-    }
-    // constant expert
-    const int ci = a.const_index[z];
-    const float* wc0 = a.const_wc + (int64_t)ci * 2 * d;
-    const float* wc1 = wc0 + d;
-    const T* vrow = reinterpret_cast<const T*>(a.const_v) + (int64_t)ci * d;
-    float xv[U][8];
-    float pa = 0.f, pb = 0.f;
-#pragma unroll
-    for (int i = 0; i < U; i++) {
-      const int u = lane + 64 * i;
-      if (u < nu) {
-        Elt<T>::load8(xrow + u * 8, xv[i]);
-        float w0[8], w1[8];
-        Elt<float>::load8(wc0 + u * 8, w0);
-        Elt<float>::load8(wc1 + u * 8, w1);
-#pragma unroll
-        for (int q = 0; q < 8; q++) {
-          pa = fmaf(w0[q], xv[i][q], pa);
-          pb = fmaf(w1[q], xv[i][q], pb);
-        }
-      }
-    }
-    pa = wave_sum(pa);
-    pb = wave_sum(pb);
-    const float mx = fmaxf(pa, pb);
-    const float ea = __expf(pa - mx), eb = __expf(pb - mx);
-    const float ca = g * (ea / (ea + eb)), cb = g * (eb / (ea + eb));
-#pragma unroll
-    for (int i = 0; i < U; i++) {
-      const int u = lane + 64 * i;
-      if (u < nu) {
-        float vv[8];
-        Elt<T>::load8(vrow + u * 8, vv);
-#pragma unroll
-        for (int q = 0; q < 8; q++) acc[i][q] += ca * xv[i][q] + cb * vv[q];
       }
     }
   }
@@ -130,56 +180,45 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 
 // ------------------------------------------------------------------------
 // Atomic stage 1: h[p] = silu(u_e . x_t) for sorted task p (task perm[p] =
-// t*k + j, e = idx[task]).  One wave walks kAtomChunk consecutive sorted
-// tasks and keeps u_e in registers while the expert repeats.
-constexpr int kAtomChunk = 8;
+// t*k + j, e = idx[task]).  A wave takes 8 consecutive sorted tasks, 8
+// lanes per task; lane s of a group loads units s, s+8, ... of both rows, so
+// each load instruction reads 8 rows x 128 contiguous bytes and a lane has
+// many loads in flight.  Consecutive tasks of one expert re-read its row
+// from cache, so the table itself streams from HBM about once.
+constexpr int kAtomTasksPerWave = 8;
 
-template <typename T, int U>
+template <typename T>
 __global__ __launch_bounds__(256) void k_atomic_h(const T* __restrict__ x,
                                                  const T* __restrict__ atom_u,
                                                  const int32_t* __restrict__ idx,
                                                  const int32_t* __restrict__ perm, int64_t n,
                                                  int k, int d, float* __restrict__ h) {
-  const int lane = threadIdx.x & 63;
-  const int64_t p0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kAtomChunk;
-  if (p0 >= n) return;
+  const int lane = threadIdx.x & 63, sub = lane & 7;
+  const int64_t p = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kAtomTasksPerWave + (lane >> 3);
+  const bool ok = p < n;
+  const int32_t task = perm[ok ? p : n - 1];
+  const int e = idx[task];
+  const T* xr = x + (int64_t)(task / k) * d;
+  const T* ur = atom_u + (int64_t)e * d;
   const int nu = d / 8;
-  float uw[U][8];
-  int cur_e = -1;
-  for (int c = 0; c < kAtomChunk; c++) {
-    const int64_t p = p0 + c;
-    if (p >= n) break;
-    const int32_t task = perm[p];
-    const int e = idx[task];
-    const int64_t tok = task / k;
-    if (e != cur_e) {
-      cur_e = e;
-      const T* ur = atom_u + (int64_t)e * d;
+  float s = 0.f;
+#pragma unroll 8
+  for (int u = sub; u < nu; u += 8) {
+    Raw8<T> xv, uv;
+    xv.load(xr + u * 8);
+    uv.load(ur + u * 8);
 #pragma unroll
-      for (int i = 0; i < U; i++) {
-        const int u = lane + 64 * i;
-        if (u < nu) Elt<T>::load8(ur + u * 8, uw[i]);
-      }
-    }
-    const T* xr = x + tok * d;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < U; i++) {
-      const int u = lane + 64 * i;
-      if (u < nu) {
-        float xv[8];
-        Elt<T>::load8(xr + u * 8, xv);
-#pragma unroll
-        for (int q = 0; q < 8; q++) s = fmaf(uw[i][q], xv[q], s);
-      }
-    }
-    s = wave_sum(s);
-    if (lane == 0) h[p] = silu_f32(s);
+    for (int q = 0; q < 8; q++) s = fmaf(uv[q], xv[q], s);
   }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  if (ok && sub == 0) h[p] = silu_f32(s);
 }
 
 // Atomic stage 2: out_t = sum_s shared + sum_j (g_tj * h_tj) w_e, one wave
-// per token, slots in order, fp32.
+// per token, slots in order, fp32.  Slot metadata and coefficients are
+// fetched one slot per lane; rows are loaded CH slots at a time.
 template <typename T, int U>
 __global__ __launch_bounds__(256) void k_atomic_combine(const T* __restrict__ atom_w,
                                                        const int32_t* __restrict__ idx,
@@ -189,6 +228,7 @@ __global__ __launch_bounds__(256) void k_atomic_combine(const T* __restrict__ at
                                                        const T* __restrict__ shared_y,
                                                        int n_shared, int64_t T_, int k, int d,
                                                        T* __restrict__ out) {
+  constexpr int CH = U >= 4 ? 2 : (U == 2 ? 4 : 8);
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
@@ -204,26 +244,44 @@ __global__ __launch_bounds__(256) void k_atomic_combine(const T* __restrict__ at
     for (int i = 0; i < U; i++) {
       const int u = lane + 64 * i;
       if (u < nu) {
-        float v[8];
-        Elt<T>::load8(row + u * 8, v);
+        Raw8<T> r;
+        r.load(row + u * 8);
 #pragma unroll
-        for (int q = 0; q < 8; q++) acc[i][q] += v[q];
+        for (int q = 0; q < 8; q++) acc[i][q] += r[q];
       }
     }
   }
-  for (int j = 0; j < k; j++) {
-    const int64_t task = t * k + j;
-    const float coef = gate[task] * h[inv_perm[task]];
-    const T* wr = atom_w + (int64_t)idx[task] * d;
+  int me = 0;
+  float mc = 0.f;
+  if (lane < k) {
+    const int64_t task = t * k + lane;
+    me = idx[task];
+    mc = gate[task] * h[inv_perm[task]];
+  }
+  for (int j0 = 0; j0 < k; j0 += CH) {
+    Raw8<T> r[CH][U];
 #pragma unroll
-    for (int i = 0; i < U; i++) {
-      const int u = lane + 64 * i;
-      if (u < nu) {
-        float v[8];
-        Elt<T>::load8(wr + u * 8, v);
+    for (int c = 0; c < CH; c++) {
+      const int j = j0 + c;
+      if (j < k) {
+        const T* wr = atom_w + (int64_t)readlane_i(me, j) * d;
 #pragma unroll
-        for (int q = 0; q < 8; q++) acc[i][q] = fmaf(coef, v[q], acc[i][q]);
+        for (int i = 0; i < U; i++) {
+          const int u = lane + 64 * i;
+          if (u < nu) r[c][i].load(wr + u * 8);
+        }
       }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+      const int j = j0 + c;
+      if (j >= k) break;
+      const float coef = readlane_f(mc, j);
+#pragma unroll
+      for (int i = 0; i < U; i++)
+        if (lane + 64 * i < nu)
+#pragma unroll
+          for (int q = 0; q < 8; q++) acc[i][q] = fmaf(coef, r[c][i][q], acc[i][q]);
     }
   }
   T* orow = out + t * d;
@@ -258,17 +316,9 @@ template <typename T>
 static hipError_t atomic_h_t(const void* x, const void* u, const int32_t* idx,
                              const int32_t* perm, int64_t n, int k, int d, float* h,
                              hipStream_t st) {
-  const int U = (int)cdiv(d, 512);
-  dim3 grid((unsigned)cdiv(cdiv(n, kAtomChunk), 4)), block(256);
-  const T* xx = (const T*)x;
-  const T* uu = (const T*)u;
-#define L(UU) hipLaunchKernelGGL((k_atomic_h<T, UU>), grid, block, 0, st, xx, uu, idx, perm, n, k, d, h)
-  if (U <= 1) L(1);
-  else if (U <= 2) L(2);
-  else if (U <= 4) L(4);
-  else if (U <= 8) L(8);
-  else L(16);
-#undef L
+  dim3 grid((unsigned)cdiv(cdiv(n, kAtomTasksPerWave), 4)), block(256);
+  hipLaunchKernelGGL((k_atomic_h<T>), grid, block, 0, st, (const T*)x, (const T*)u, idx, perm, n,
+                     k, d, h);
   return hipGetLastError();
 }
 

@@ -66,6 +66,103 @@ __global__ __launch_bounds__(1024) void k_scan_single_block(const int32_t* in, i
   if (write_total && tid == 1023) out[n] = part[1023];
 }
 
+// Multi-block exclusive scan for long arrays: each block of 256 threads
+// covers 4096 consecutive ints (16 per thread, loaded as four 16-byte
+// vectors); pass 1 writes block totals, the totals are scanned by one
+// block, pass 2 rescans each block locally and adds its offset.
+constexpr int kScanThreads = 256;
+constexpr int kScanPer = 16;
+constexpr int kScanTile = kScanThreads * kScanPer;
+
+__device__ __forceinline__ int32_t block_exclusive_sum(int32_t v, int32_t* lds_w, int32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int32_t t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) lds_w[w] = inc;
+  __syncthreads();
+  int32_t wbase = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < kScanThreads / 64; i++) {
+    const int32_t t = lds_w[i];
+    if (i < w) wbase += t;
+    total += t;
+  }
+  return wbase + inc - v;
+}
+
+__device__ __forceinline__ void load16(const int32_t* in, int64_t n, int64_t base, int32_t v[16]) {
+  if (base + 16 <= n && ((uintptr_t)(in + base) & 15) == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      int4 t = reinterpret_cast<const int4*>(in + base)[q];
+      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = base + i < n ? in[base + i] : 0;
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_totals(const int32_t* __restrict__ in,
+                                                              int64_t n,
+                                                              int32_t* __restrict__ totals) {
+  __shared__ int32_t lds_w[kScanThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kScanPer;
+  int32_t v[16];
+  load16(in, n, base, v);
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) s += v[i];
+  int32_t total;
+  block_exclusive_sum(s, lds_w, total);
+  if (threadIdx.x == 0) totals[blockIdx.x] = total;
+}
+
+// out may alias in.  offsets: scanned block totals (nullptr: one block).
+__global__ __launch_bounds__(kScanThreads) void k_scan_finish(const int32_t* in, int32_t* out,
+                                                              int64_t n,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int32_t* total_out) {
+  __shared__ int32_t lds_w[kScanThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kScanPer;
+  int32_t v[16];
+  load16(in, n, base, v);
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) s += v[i];
+  int32_t total;
+  int32_t run = block_exclusive_sum(s, lds_w, total) + (offsets ? offsets[blockIdx.x] : 0);
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    if (base + i < n) out[base + i] = run;
+    run += v[i];
+  }
+  if (total_out && blockIdx.x == gridDim.x - 1 && threadIdx.x == 0)
+    *total_out = (offsets ? offsets[blockIdx.x] : 0) + total;
+}
+
+// exclusive scan of n ints (in may equal out); writes *total_out when given.
+// scratch: cdiv(n, 4096) + 1 ints.
+static void exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* total_out,
+                           int32_t* scratch, hipStream_t st) {
+  const int64_t nblk = cdiv(n, kScanTile);
+  if (nblk <= 1) {
+    hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kScanThreads), 0, st, in, out, n,
+                       (const int32_t*)nullptr, total_out);
+    return;
+  }
+  hipLaunchKernelGGL(k_scan_totals, dim3((unsigned)nblk), dim3(kScanThreads), 0, st, in, n,
+                     scratch);
+  hipLaunchKernelGGL(k_scan_single_block, dim3(1), dim3(1024), 0, st, scratch, scratch, nblk, 0);
+  hipLaunchKernelGGL(k_scan_finish, dim3((unsigned)nblk), dim3(kScanThreads), 0, st, in, out, n,
+                     (const int32_t*)scratch, total_out);
+}
+
 // Single-pass dispatch (E <= 256): exclusive scan of the digit-major tile
 // histogram in place, and from it the expert offsets (the scanned value at
 // (e, tile 0)) and counts.
@@ -186,8 +283,10 @@ int64_t dispatch_scratch_ints(int64_t n, int E) {
   while ((1ll << bits) < E) bits++;
   int passes = bits ? (bits + 7) / 8 : 1;
   int64_t nb = cdiv(n, kRadixTile);
-  // hist (256 * nb) + one temp array of n for multi-pass sorts
-  return 256 * nb + (passes > 1 ? n : 0);
+  // hist (256 * nb) + for multi-pass sorts one temp array of n and the
+  // scan's block totals
+  const int64_t scan = cdiv((256 * nb > E ? 256 * nb : E), kScanTile) + 1;
+  return 256 * nb + (passes > 1 ? n + scan : 0);
 }
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
@@ -222,8 +321,8 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
                      (int64_t)E);
   hipLaunchKernelGGL(k_count_experts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, idx, n, E,
                      counts);
-  hipLaunchKernelGGL(k_scan_single_block, dim3(1), dim3(1024), 0, st, counts, offsets,
-                     (int64_t)E, 1);
+  int32_t* scan_scratch = tmp + n;
+  exclusive_scan(counts, offsets, (int64_t)E, offsets + E, scan_scratch, st);
   const int passes = (bits + 7) / 8;
   const int32_t* src = nullptr;
   for (int p = 0; p < passes; p++) {
@@ -234,8 +333,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     int32_t* dst = ((passes - 1 - p) % 2) ? tmp : perm;
     hipLaunchKernelGGL(k_radix_hist, dim3(nb), dim3(kRadixThreads), 0, st, idx, src, n, shift,
                        pb, hist, nb);
-    hipLaunchKernelGGL(k_scan_single_block, dim3(1), dim3(1024), 0, st, hist, hist,
-                       (int64_t)(1 << pb) * nb, 0);
+    exclusive_scan(hist, hist, (int64_t)(1 << pb) * nb, (int32_t*)nullptr, scan_scratch, st);
     hipLaunchKernelGGL(k_radix_scatter, dim3(nb), dim3(kRadixThreads), 0, st, idx, src, n, shift,
                        pb, hist, nb, dst, last ? inv_perm : (int32_t*)nullptr);
     src = dst;

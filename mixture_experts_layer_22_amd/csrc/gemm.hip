@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
     if (more) {
       // tile kt+1 has landed for every wave, and every wave has finished
       // reading tile kt from LDS (its reads completed before this barrier)
-      if (steady) wait_vmcnt<2 * LOADS>();
+      if (steady) wait_vmcnt<(STAGES - 2) * LOADS>();
       else wait_tile(kt + 1, kt + STAGES - 1);
       __builtin_amdgcn_s_barrier();
     }

@@ -33,62 +33,75 @@ __global__ void k_split_router(const float* __restrict__ W, uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------------
-// logits[t, col_off + n] = x[t, x_off : x_off+K] . W[n, :K]   (n < NL)
-// bf16 x, W given as the three bf16 slices W3[p * slice + n * K + kk].
-// Block: 16 tokens x 64 logits, 4 waves of 16x16 (v_mfma_f32_16x16x32_bf16);
-// grid (ceil(T/16), ceil(NL/64)).  Operands go straight from global memory
-// to MFMA registers: per 64-wide K block, lane (r = l%16, q = l/16) loads 16
-// consecutive elements of its row at q*16 and MFMA step s uses elements
-// [q*16 + 8s, +8).  A and B share that K permutation, so the dot products
+// Partial logits over a K range:
+//   part[z][t, col_off + n] = x[t, x_off + K_z] . W[n, K_z]   (n < NL)
+// with K_z the z-th of gridDim.z equal K ranges (split K keeps enough
+// waves busy at small T; the selection kernel adds the partials in order z).
+// bf16 x; W given as three bf16 slices W3[p * slice + n * K + kk].
+// Block: 64 tokens x 64 logits, wave w owns logits 16w..16w+15 for all 64
+// tokens (4 v_mfma_f32_16x16x32_bf16 tiles), so every weight fragment is
+// used for 64 tokens.  Operands go straight from global memory to MFMA
+// registers: per 64-wide K block, lane (r = l%16, q = l/16) loads 16
+// consecutive elements of its row at q*16 and MFMA step h uses elements
+// [q*16 + 8h, +8).  A and B share that K permutation, so the dot products
 // are unchanged while every row is read as one 128-byte run.  The three
 // weight slices accumulate into one fp32 accumulator.
 __global__ __launch_bounds__(256) void k_router_logits_bf16(
     const uint16_t* __restrict__ x, int64_t T, int ldx, int x_off,
     const uint16_t* __restrict__ W3, int64_t slice, int NL, int K,
-    float* __restrict__ logits, int ldl, int col_off) {
+    float* __restrict__ logits, int ldl, int col_off, int64_t part_stride) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
   const int n0 = blockIdx.y * 64 + wave * 16;
   if (n0 >= NL) return;
+  const int kc = K / gridDim.z;
+  const int kbeg = blockIdx.z * kc, kend = kbeg + kc;
   const int r = lane & 15, q = lane >> 4;
-  const int64_t am = m0 + r;
-  const int bn = n0 + r;
-  const bool a_ok = am < T, b_ok = bn < NL;
-  const uint16_t* ap = x + (a_ok ? am : 0) * (int64_t)ldx + x_off + q * 16;
-  const uint16_t* bp = W3 + (int64_t)(b_ok ? bn : 0) * K + q * 16;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int kb = 0; kb < K; kb += 64) {
-    u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-    if (a_ok) {
-      a0 = *reinterpret_cast<const u32x4*>(ap + kb);
-      a1 = *reinterpret_cast<const u32x4*>(ap + kb + 8);
-    }
-    u32x4 b0[3], b1[3];
+  const uint16_t* ap[4];
 #pragma unroll
-    for (int p = 0; p < 3; p++) {
-      b0[p] = u32x4{0, 0, 0, 0};
-      b1[p] = u32x4{0, 0, 0, 0};
-      if (b_ok) {
-        b0[p] = *reinterpret_cast<const u32x4*>(bp + p * slice + kb);
-        b1[p] = *reinterpret_cast<const u32x4*>(bp + p * slice + kb + 8);
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 3; p++) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
-                                                    __builtin_bit_cast(bf16x8, b0[p]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
-                                                    __builtin_bit_cast(bf16x8, b1[p]), acc, 0, 0, 0);
-    }
+  for (int i = 0; i < 4; i++) {
+    int64_t m = m0 + 16 * i + r;
+    if (m >= T) m = T - 1;  // clamped rows feed only outputs that are not stored
+    ap[i] = x + m * (int64_t)ldx + x_off + q * 16;
   }
-  // lane holds C[4 q + j][r]
+  const int bn = n0 + r < NL ? n0 + r : NL - 1;
+  const uint16_t* bp = W3 + (int64_t)bn * K + q * 16;
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int kb = kbeg; kb < kend; kb += 64) {
+    u32x4 a[4][2], b[3][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      a[i][0] = *reinterpret_cast<const u32x4*>(ap[i] + kb);
+      a[i][1] = *reinterpret_cast<const u32x4*>(ap[i] + kb + 8);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; p++) {
+      b[p][0] = *reinterpret_cast<const u32x4*>(bp + p * slice + kb);
+      b[p][1] = *reinterpret_cast<const u32x4*>(bp + p * slice + kb + 8);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; p++)
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][h]),
+                                                           __builtin_bit_cast(bf16x8, b[p][h]),
+                                                           acc[i], 0, 0, 0);
+  }
+  // lane holds C[16 i + 4 q + j][r]
   const int n = n0 + r;
+  float* out = logits + blockIdx.z * part_stride;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int64_t m = m0 + 4 * q + j;
-    if (m < T && n < NL) logits[m * ldl + col_off + n] = acc[j];
-  }
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int64_t m = m0 + 16 * i + 4 * q + j;
+      if (m < T && n < NL) out[m * ldl + col_off + n] = acc[i][j];
+    }
 }
 
 // fp32 layers: one thread per logit, four interleaved fp32 partial sums.
@@ -117,7 +130,8 @@ __global__ void k_router_logits_f32(const float* __restrict__ x, int64_t T, int 
 // experts.  Order (-l, e); gates = softmax over all E at the chosen ones,
 // optionally renormalised over the k.
 template <int V>
-__global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ logits, int64_t T,
+__global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ logits, int nparts,
+                                                    int64_t part_stride, int64_t T,
                                                     int E, int E_ffn, int k, float tau,
                                                     const float* __restrict__ bias, int renorm,
                                                     int32_t* __restrict__ idx_out,
@@ -133,6 +147,7 @@ __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ l
     float l = -INFINITY;
     if (e < E) {
       l = row[e];
+      for (int z = 1; z < nparts; z++) l += row[z * part_stride + e];
       if (bias) l = l + bias[e];
       if (e < E_ffn) l = tau * l;
     }
@@ -181,7 +196,8 @@ __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ l
 //   3. top-k candidates by (-sigma, id); gates = softmax over the k sigmas.
 // V = values per lane (max(rows, cols, krow*kcol) <= 64 V); krow, kcol <= 64.
 template <int V>
-__global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ scores, int64_t T,
+__global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ scores, int nparts,
+                                                  int64_t part_stride, int64_t T,
                                                   int rows, int cols, int krow, int kcol, int k,
                                                   int32_t* __restrict__ idx_out,
                                                   float* __restrict__ gate_out) {
@@ -200,7 +216,12 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
 #pragma unroll
     for (int i = 0; i < V; i++) {
       int e = lane + 64 * i;
-      v[i] = e < n ? s[e] : -INFINITY;
+      float sc = -INFINITY;
+      if (e < n) {
+        sc = s[e];
+        for (int z = 1; z < nparts; z++) sc += s[z * part_stride + e];
+      }
+      v[i] = sc;
     }
     uint32_t taken = 0;
     for (int j = 0; j < kk; j++) {
@@ -274,14 +295,23 @@ hipError_t launch_split_router(const float* W, uint16_t* W3, int64_t n, hipStrea
   return hipGetLastError();
 }
 
+int router_splits(int dtype, int64_t T, int NL, int K) {
+  if (dtype != MOE_BF16) return 1;
+  const int64_t blocks = cdiv(T, 64) * cdiv(NL, 64);
+  int S = 1;
+  while (S < 8 && blocks * S < 256 && K % (64 * 2 * S) == 0) S *= 2;
+  return S;
+}
+
 hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, int x_off,
                                 const void* W, int64_t slice, int NL, int K, float* logits,
-                                int ldl, int col_off, hipStream_t st) {
+                                int ldl, int col_off, int splits, hipStream_t st) {
   if (T == 0 || NL == 0) return hipSuccess;
   if (dtype == MOE_BF16) {
-    dim3 grid((unsigned)cdiv(T, 16), (unsigned)cdiv(NL, 64));
+    dim3 grid((unsigned)cdiv(T, 64), (unsigned)cdiv(NL, 64), (unsigned)splits);
     hipLaunchKernelGGL(k_router_logits_bf16, grid, dim3(256), 0, st, (const uint16_t*)x, T, ldx,
-                       x_off, (const uint16_t*)W, slice, NL, K, logits, ldl, col_off);
+                       x_off, (const uint16_t*)W, slice, NL, K, logits, ldl, col_off,
+                       (int64_t)T * ldl);
   } else {
     hipLaunchKernelGGL(k_router_logits_f32, dim3((unsigned)cdiv(T * NL, 256)), dim3(256), 0, st,
                        (const float*)x, T, ldx, x_off, (const float*)W, NL, K, logits, ldl,
@@ -290,14 +320,14 @@ hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, in
   return hipGetLastError();
 }
 
-hipError_t launch_select_topk(const float* logits, int64_t T, int E, int E_ffn, int k, float tau,
-                              const float* bias, int renorm, int32_t* idx, float* gate,
+hipError_t launch_select_topk(const float* logits, int splits, int64_t T, int E, int E_ffn, int k,
+                              float tau, const float* bias, int renorm, int32_t* idx, float* gate,
                               hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv(T, 4)), block(256);
   int V = (int)cdiv(E, 64);
-#define SEL(VV) hipLaunchKernelGGL(k_select_topk<VV>, grid, block, 0, st, logits, T, E, E_ffn, k, \
-                                   tau, bias, renorm, idx, gate)
+#define SEL(VV) hipLaunchKernelGGL(k_select_topk<VV>, grid, block, 0, st, logits, splits, \
+                                   (int64_t)T * E, T, E, E_ffn, k, tau, bias, renorm, idx, gate)
   if (V <= 1) SEL(1);
   else if (V <= 2) SEL(2);
   else SEL(4);
@@ -305,16 +335,17 @@ hipError_t launch_select_topk(const float* logits, int64_t T, int E, int E_ffn, 
   return hipGetLastError();
 }
 
-hipError_t launch_select_pk(const float* scores, int64_t T, int rows, int cols, int krow, int kcol,
-                            int k, int32_t* idx, float* gate, hipStream_t st) {
+hipError_t launch_select_pk(const float* scores, int splits, int64_t T, int rows, int cols,
+                            int krow, int kcol, int k, int32_t* idx, float* gate, hipStream_t st) {
   if (T == 0) return hipSuccess;
   int64_t mx = rows;
   if (cols > mx) mx = cols;
   if ((int64_t)krow * kcol > mx) mx = (int64_t)krow * kcol;
   int V = (int)cdiv(mx, 64);
   dim3 grid((unsigned)cdiv(T, 4)), block(256);
-#define SEL(VV) hipLaunchKernelGGL(k_select_pk<VV>, grid, block, 0, st, scores, T, rows, cols, krow, \
-                                   kcol, k, idx, gate)
+#define SEL(VV) hipLaunchKernelGGL(k_select_pk<VV>, grid, block, 0, st, scores, splits, \
+                                   (int64_t)T * (rows + cols), T, rows, cols, krow, kcol, k, idx, \
+                                   gate)
   if (V <= 1) SEL(1);
   else if (V <= 2) SEL(2);
   else if (V <= 4) SEL(4);
