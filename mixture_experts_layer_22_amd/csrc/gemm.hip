@@ -269,34 +269,36 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
-  constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
+// One tile of BMT (256 or 128) rows x 256 B rows.  Waves form a 2 x 2
+// grid; a wave owns BMT/2 rows and 128 B rows (FM x 4 fragments of 32x32).
+template <int BMT, bool SWIGLU>
+__device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx<SWIGLU>& c,
+                                             int n0, uint16_t* lds) {
+  constexpr int BM = 256;                      // LDS layout: A rows [0, 256), B rows after
+  constexpr int BN = 256, BK = 32, STAGES = 4;
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
-  constexpr int FM = 4, FN = 4;                // 32x32 fragments per wave (2 x 2 waves)
+  constexpr int FM = BMT / 64, FN = 4;
   constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 16384 bf16 = 32 KB
-  constexpr int LOADS = 8;                     // 1 KB copies per wave per K tile
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE_ELEMS];
-
-  int tile_id, n_tile;
-  if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
-  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
-  const int n0 = n_tile * BNO;
-  if (n0 >= c.N) return;
+  constexpr int LA = BMT / 64;                 // A copies (1 KB = 16 rows) per wave per K tile
+  constexpr int LOADS = LA + 4;                // + 4 B copies
+  constexpr int NQ = (FM + FN) * 2;            // fragments per K tile
+  constexpr int NG = FM * FN / 2;              // groups of 4 MFMAs per K tile
+  static_assert(BNO == (SWIGLU ? 128 : 256), "tile");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // loader: copy j (0..7) of this wave covers tile rows (wave*4 + j%4)*16 +
-  // lane/4 of A (j < 4) or B (j >= 4); the lane's 16 B is logical chunk
-  // (lane & 3) ^ f(row) of that row.
+  // loader: copy j < LA covers A rows (wave*LA + j)*16 + lane/4, copy j >= LA
+  // covers B rows (wave*4 + j-LA)*16 + lane/4; the lane's 16 B is logical
+  // chunk (lane & 3) ^ f(row) of that row.
   const uint16_t* src[LOADS];
 #pragma unroll
   for (int j = 0; j < LOADS; j++) {
-    const int row = (wave * 4 + (j & 3)) * 16 + (lane >> 2);
+    const bool isa = j < LA;
+    const int row = (isa ? (wave * LA + j) : (wave * 4 + j - LA)) * 16 + (lane >> 2);
     const int chunk = (lane & 3) ^ lds_swz(row);
     const uint16_t* p;
-    if (j < 4) {
+    if (isa) {
       p = a_row<uint16_t, SWIGLU>(args, c, row);
       if (!p) p = a_row<uint16_t, SWIGLU>(args, c, 0);
     } else {
@@ -307,7 +309,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
   }
   auto copy_one = [&](int kt, int j) {
     uint16_t* st = lds + (kt % STAGES) * STAGE_ELEMS;
-    const int row0 = (j < 4 ? 0 : BM) + (wave * 4 + (j & 3)) * 16;
+    const bool isa = j < LA;
+    const int row0 = isa ? (wave * LA + j) * 16 : BM + (wave * 4 + j - LA) * 16;
     dl_copy16(src[j] + kt * BK, st + row0 * BK);
   };
 
@@ -336,13 +339,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
 
   // fragments of one K tile (two 16-wide MFMA steps), double buffered in
   // registers: tile kt+1 is read from LDS while tile kt is multiplied.
-  // Fragment q (0..15) of a tile: step q / 8, then A rows (q%8 < 4) or B rows.
-  bf16x8 fr[2][16];
+  // Fragment q of a tile: step q / (FM+FN), then A (index < FM) or B.
+  bf16x8 fr[2][NQ];
   auto read_frag = [&](int kt, int buf, int q) {
     const uint16_t* st = lds + (kt % STAGES) * STAGE_ELEMS;
-    const int s = q >> 3, i = q & 7;
+    const int s = q / (FM + FN), i = q % (FM + FN);
     const int ch = ((2 * s + fhalf) ^ fsw) * 8;
-    const int row = i < 4 ? (wm * FM + i) * 32 + frow : BM + brow[i - 4] + frow;
+    const int row = i < FM ? (wm * FM + i) * 32 + frow : BM + brow[i - FM] + frow;
     fr[buf][q] = *reinterpret_cast<const bf16x8*>(st + row * BK + ch);
   };
   auto wait_tile = [&](int t, int issued_upto) {
@@ -362,13 +365,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
   wait_tile(0, STAGES - 1);
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int q = 0; q < 16; q++) read_frag(0, 0, q);
+  for (int q = 0; q < NQ; q++) read_frag(0, 0, q);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
-  // One K tile: make tile kt+1 visible, then 8 groups of {one copy of tile
-  // kt+STAGES into tile kt's stage, two fragment reads of tile kt+1, four
-  // MFMAs of tile kt}, so the copy issue and LDS reads are spread over the
-  // MFMA stream.
+  // One K tile: make tile kt+1 visible, then NG groups of {copies of tile
+  // kt+STAGES into tile kt's stage, fragment reads of tile kt+1, four MFMAs
+  // of tile kt}, so copy issue and LDS reads are spread over the MFMAs.
   auto step = [&](int kt, auto buf_c, auto steady_c) {
     constexpr int buf = decltype(buf_c)::value;
     constexpr bool steady = decltype(steady_c)::value;  // copies and reads all valid
@@ -382,19 +384,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
       __builtin_amdgcn_s_barrier();
     }
 #pragma unroll
-    for (int g = 0; g < 8; g++) {
-      if (refill) copy_one(kt + STAGES, g);
-      if (more) {
-        read_frag(kt + 1, buf ^ 1, 2 * g);
-        read_frag(kt + 1, buf ^ 1, 2 * g + 1);
-      }
-      // MFMAs 4g .. 4g+3 of this tile: step s = g / 4, A fragment fm = g % 4
-      const int s = g >> 2, fm = g & 3;
+    for (int g = 0; g < NG; g++) {
+      if (refill)
 #pragma unroll
-      for (int fn = 0; fn < FN; fn++)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][8 * s + 4 + fn],
-                                                              fr[buf][8 * s + fm], acc[fm][fn],
-                                                              0, 0, 0);
+        for (int j = g * LOADS / NG; j < (g + 1) * LOADS / NG; j++) copy_one(kt + STAGES, j);
+      if (more)
+#pragma unroll
+        for (int q = g * NQ / NG; q < (g + 1) * NQ / NG; q++) read_frag(kt + 1, buf ^ 1, q);
+#pragma unroll
+      for (int m = 4 * g; m < 4 * g + 4; m++) {
+        const int s = m / (FM * FN), fm = (m / FN) % FM, fn = m % FN;
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            fr[buf][s * (FM + FN) + FM + fn], fr[buf][s * (FM + FN) + fm], acc[fm][fn], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): next tile's fragments are in registers
@@ -404,23 +406,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
   // still has a refill) runs without per-group conditions.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using Steady = std::true_type;
-  using Tail = std::false_type;
   int kt = 0;
   for (; kt + STAGES < nk; kt += 2) {
-    step(kt, I0{}, Steady{});
-    step(kt + 1, I1{}, Steady{});
+    step(kt, I0{}, std::true_type{});
+    step(kt + 1, I1{}, std::true_type{});
   }
   for (; kt < nk; kt += 2) {
-    step(kt, I0{}, Tail{});
-    step(kt + 1, I1{}, Tail{});
+    step(kt, I0{}, std::false_type{});
+    step(kt + 1, I1{}, std::false_type{});
   }
 
-  // epilogue.  acc[fm][fn][j] = C[row = (wm*FM + fm)*32 + lane%32]
-  //                              [col = fn*32 + 8(j/4) + 4(lane/32) + j%4]
+  // epilogue.  acc[fm][fn][e] = C[row = (wm*FM + fm)*32 + lane%32]
+  //                              [col = fn*32 + 8(e/4) + 4(lane/32) + e%4]
   // (col relative to the wave's first column).  Full tiles skip the bounds
   // checks; every store writes 4 consecutive bf16 columns.
-  const bool full_rows = c.nr >= BM;
+  const bool full_rows = c.nr >= BMT;
   const bool full_cols = n0 + BNO <= c.N;
 #pragma unroll
   for (int fm = 0; fm < FM; fm++) {
@@ -461,6 +461,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
         }
     }
   }
+}
+
+// A tile of at most 128 valid rows runs the half-height variant, so groups
+// with few tokens (the long tail of expert loads) waste half the MFMA work
+// of a 256-row tile instead of most of it.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * (256 + 256) * 32];
+  int tile_id, n_tile;
+  if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
+  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
+  const int n0 = n_tile * (SWIGLU ? 128 : 256);
+  if (n0 >= c.N) return;
+  if (c.nr > 128)
+    gemm_tile_dl<256, SWIGLU>(args, c, n0, lds);
+  else
+    gemm_tile_dl<128, SWIGLU>(args, c, n0, lds);
 }
 
 // ------------------------------------------------------------------------
