@@ -85,17 +85,32 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Cross-lane reductions with DPP: xor 1 and xor 2 inside quads, rotations
+// by 4 and 8 inside rows of 16 lanes, then the four row results read into
+// scalars.  Every lane returns the wave-wide result.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce_dpp(T v, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  int b = __builtin_bit_cast(int, v);
+  b = __builtin_bit_cast(int, op(v, __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false))));
+  b = __builtin_bit_cast(int, op(__builtin_bit_cast(T, b), __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false))));
+  b = __builtin_bit_cast(int, op(__builtin_bit_cast(T, b), __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(b, b, 0x124, 0xF, 0xF, false))));
+  b = __builtin_bit_cast(int, op(__builtin_bit_cast(T, b), __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(b, b, 0x128, 0xF, 0xF, false))));
+  const T r0 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 0));
+  const T r1 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 16));
+  const T r2 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 32));
+  const T r3 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
 // (value, index) argmax across the wave: larger value wins, ties go to the
-// smaller index.  Every lane returns the winner.
+// smaller index.  Every lane returns the winner.  NaN values are not
+// supported (routing of NaN inputs is unspecified).
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    float ov = __shfl_xor(v, o, kWave);
-    int oi = __shfl_xor(i, o, kWave);
-    bool take = (ov > v) || (ov == v && oi < i);
-    v = take ? ov : v;
-    i = take ? oi : i;
-  }
+  const float m = wave_reduce_dpp(v, [](float a, float b) { return fmaxf(a, b); });
+  const int cand = (v == m) ? i : 0x7fffffff;
+  i = wave_reduce_dpp(cand, [](int a, int b) { return a < b ? a : b; });
+  v = m;
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

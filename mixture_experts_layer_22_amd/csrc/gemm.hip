@@ -481,36 +481,68 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
 }
 
 // ------------------------------------------------------------------------
-// fp32 layers: plain FMA, one thread per output element, 32-row tiles.
+// fp32 layers: 32-row x 64-column output tiles on plain FMA.  K advances in
+// chunks of 32 staged through LDS (A 32 x 32, B 64 x 32; for the gated GEMM
+// the gate and up rows of the 64 columns); thread (r = tid / 8, c = tid % 8)
+// accumulates row r, columns c, c+8, ..., c+56.
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
+  constexpr int KC = 32;
+  constexpr int NB = SWIGLU ? 128 : 64;   // B rows staged per chunk
+  __shared__ float sa[32][KC + 1];
+  __shared__ float sb[NB][KC + 1];
   int tile_id, n_tile;
   if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
   const int n0 = n_tile * 64;
   if (n0 >= c.N) return;
-  const int i = threadIdx.x >> 3;  // local row 0..31
-  if (i >= c.nr) return;
-  const float* a = a_row<float, SWIGLU>(args, c, i);
-  float* out = c_row<float, SWIGLU>(args, c, i);
-  for (int jj = threadIdx.x & 7; jj < 64; jj += 8) {
-    const int n = n0 + jj;
-    if (n >= c.N) break;
-    if (SWIGLU) {
-      const float* g = b_row<float, SWIGLU, 2>(args, c, n, 0);
-      const float* u = b_row<float, SWIGLU, 2>(args, c, n, 1);
-      float sg = 0.f, su = 0.f;
-      for (int kk = 0; kk < c.K; kk++) {
-        sg = fmaf(a[kk], g[kk], sg);
-        su = fmaf(a[kk], u[kk], su);
-      }
-      out[n] = silu_f32(sg) * su;
-    } else {
-      const float* b = b_row<float, SWIGLU, 1>(args, c, n, 0);
-      float s = 0.f;
-      for (int kk = 0; kk < c.K; kk++) s = fmaf(a[kk], b[kk], s);
-      out[n] = s;
+  const int tid = threadIdx.x;
+  const int r = tid >> 3, cc = tid & 7;
+  float acc[8], acc2[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) { acc[j] = 0.f; acc2[j] = 0.f; }
+  // loader: A row tid/8 (4 floats at (tid%8)*4); B rows tid/8 + 32 q
+  const float* arow = a_row<float, SWIGLU>(args, c, r);
+  const float* brow[NB / 32];
+#pragma unroll
+  for (int q = 0; q < NB / 32; q++) {
+    const int j = r + 32 * q;  // 0 .. NB-1
+    const float* p = SWIGLU ? b_row<float, SWIGLU, 128>(args, c, n0, j)
+                            : b_row<float, SWIGLU, 64>(args, c, n0, j);
+    brow[q] = p;
+  }
+  for (int k0 = 0; k0 < c.K; k0 += KC) {
+    {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (arow) v = *reinterpret_cast<const f32x4*>(arow + k0 + cc * 4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) sa[r][cc * 4 + e] = v[e];
     }
+#pragma unroll
+    for (int q = 0; q < NB / 32; q++) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (brow[q]) v = *reinterpret_cast<const f32x4*>(brow[q] + k0 + cc * 4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) sb[r + 32 * q][cc * 4 + e] = v[e];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < KC; kk++) {
+      const float av = sa[r][kk];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        acc[j] = fmaf(av, sb[cc + 8 * j][kk], acc[j]);
+        if (SWIGLU) acc2[j] = fmaf(av, sb[64 + cc + 8 * j][kk], acc2[j]);
+      }
+    }
+    __syncthreads();
+  }
+  if (r >= c.nr) return;
+  float* out = c_row<float, SWIGLU>(args, c, r);
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int n = n0 + cc + 8 * j;
+    if (n < c.N) out[n] = SWIGLU ? silu_f32(acc[j]) * acc2[j] : acc[j];
   }
 }
 
