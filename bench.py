@@ -23,6 +23,21 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (datasheet)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (datasheet)
 METRIC = "MoE layer tokens/sec at 1 GPU; % of bf16 MFMA peak or HBM GB/s"
+COPY_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def measured_traffic(workload, kernel_sha):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_sha:
+        return None
+    return rec.get("bytes")
 
 
 def log(*a):
@@ -82,6 +97,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="deepseek16b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy a 1 GiB device buffer three times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -91,6 +108,17 @@ def main():
     import torch
     from mixture_experts_layer_22_amd import binding as B
     from mixture_experts_layer_22_amd import inputs as I
+    from mixture_experts_layer_22_amd import profiling as P
+
+    if args.calibrate_copy:
+        n = COPY_BYTES // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+        return
 
     cfg = I.CONFIGS[args.workload]
     log(f"[bench] workload {cfg.name}: generating inputs")
@@ -161,6 +189,7 @@ def main():
         roof = {"bound": "mfma", "kernel": "k_grouped_gemm_bf16 (GEMM1 + SiLU gate)",
                 "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+    roof["traffic"] = measured_traffic(cfg.name, P.kernel_source_sha())
     expert_flop = work["expert1_flop"] + work["expert2_flop"]
     line = {
         "metric": METRIC,

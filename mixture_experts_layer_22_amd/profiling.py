@@ -1,0 +1,124 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+    python -m mixture_experts_layer_22_amd.profiling stats  DIR  [--out FILE] [--cmd CMD]
+    python -m mixture_experts_layer_22_amd.profiling traffic --kernel NAME
+           --copy-fetch DIR --copy-write DIR --fetch DIR --write DIR
+           [--copy-bytes N] [--out FILE] [--cmd CMD]
+
+`stats` turns a `--kernel-trace --stats` run (CSV output) into a short text
+table.  `traffic` turns two counter runs of a workload (FETCH_SIZE, then
+WRITE_SIZE) into HBM bytes per launch of one kernel, each scaled by what the
+same counter reads for a plain device copy of known size (the copy moves
+copy_bytes in and copy_bytes out), and writes a JSON record that bench.py
+reports as roofline.traffic while the kernel source is unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_sha(path: str = os.path.join(HERE, "csrc", "gemm.hip")) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _one(pattern):
+    hits = glob.glob(pattern, recursive=True)
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def stats_table(run_dir: str, top: int = 20) -> str:
+    rows = list(csv.DictReader(open(_one(os.path.join(run_dir, "**", "*kernel_stats.csv")))))
+    lines = [f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in rows[:top]:
+        lines.append(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
+                     f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} "
+                     f"{float(r['Percentage']):6.2f}")
+    return "\n".join(lines)
+
+
+def counter_per_dispatch(run_dir: str, counter: str, kernel_substr: str, reduce: str = "mean"):
+    """Mean (or max) over dispatches of kernel `kernel_substr` of the counter
+    summed over its instances (FETCH_SIZE / WRITE_SIZE are in KiB)."""
+    rows = csv.DictReader(open(_one(os.path.join(run_dir, "**", "*counter_collection.csv"))))
+    per = collections.defaultdict(float)
+    for r in rows:
+        if r["Counter_Name"] != counter or kernel_substr not in r["Kernel_Name"]:
+            continue
+        per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} rows for kernel {kernel_substr!r} in {run_dir}")
+    vals = list(per.values())
+    if reduce == "max":
+        return max(vals), len(vals)
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_record(kernel, copy_fetch, copy_write, fetch, write, copy_bytes, copy_kernel="copy"):
+    # the copy run also moves small buffers; the calibration copy is the largest
+    cf, _ = counter_per_dispatch(copy_fetch, "FETCH_SIZE", copy_kernel, "max")
+    cw, _ = counter_per_dispatch(copy_write, "WRITE_SIZE", copy_kernel, "max")
+    f, nf = counter_per_dispatch(fetch, "FETCH_SIZE", kernel)
+    w, nw = counter_per_dispatch(write, "WRITE_SIZE", kernel)
+    fetch_scale = copy_bytes / (cf * 1024.0)
+    write_scale = copy_bytes / (cw * 1024.0)
+    return {
+        "kernel": kernel,
+        "fetch_bytes": f * 1024.0 * fetch_scale,
+        "write_bytes": w * 1024.0 * write_scale,
+        "bytes": f * 1024.0 * fetch_scale + w * 1024.0 * write_scale,
+        "fetch_kib_raw": f, "write_kib_raw": w,
+        "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": copy_bytes,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "dispatches": [nf, nw],
+        "source_sha256": kernel_source_sha(),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--out")
+    s.add_argument("--cmd", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=int, default=1 << 30)
+    t.add_argument("--copy-kernel", default="copy")
+    t.add_argument("--out")
+    t.add_argument("--cmd", default="")
+    a = ap.parse_args(argv)
+    if a.cmd_name == "stats":
+        text = stats_table(a.dir)
+        if a.cmd:
+            text = f"command: {a.cmd}\n\n{text}\n"
+    else:
+        rec = traffic_record(a.kernel, a.copy_fetch, a.copy_write, a.fetch, a.write, a.copy_bytes,
+                             a.copy_kernel)
+        if a.cmd:
+            rec["command"] = a.cmd
+        text = json.dumps(rec, indent=1)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text + ("\n" if not text.endswith("\n") else ""))
+    print(text)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
