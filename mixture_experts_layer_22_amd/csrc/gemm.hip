@@ -271,32 +271,47 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One tile of BMT (256 or 128) rows x 256 B rows.  Waves form a 2 x 2
 // grid; a wave owns BMT/2 rows and 128 B rows (FM x 4 fragments of 32x32).
+//
+// K advances in 64-wide tiles held in two LDS stages of 64 KB (A rows
+// [0, 256), B rows [256, 512), 128 B per row).  A K tile is four 16-wide
+// MFMA steps.  Fragments of step s+1 are read while step s multiplies
+// (double buffered in registers).  Between steps 2 and 3 one barrier both
+// publishes tile kt+1 (its copies were issued a whole tile earlier) and
+// frees tile kt's stage, which the copies of tile kt+2 refill during step 3;
+// step 3 also reads tile kt+1's first fragments.  One barrier per 64 MFMAs.
+//
+// LDS rows are 8 chunks of 16 B; chunk c of row r sits at c ^ f(r) with
+// f(r) = (r & 7) ^ ((r >> 3) & 1): a fragment read (32 consecutive rows,
+// one chunk) hits distinct banks within every 8 lanes (32 banks) and every
+// 16 lanes (64 banks).
+__device__ __forceinline__ int lds_swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 template <int BMT, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx<SWIGLU>& c,
                                              int n0, uint16_t* lds) {
   constexpr int BM = 256;                      // LDS layout: A rows [0, 256), B rows after
-  constexpr int BN = 256, BK = 32, STAGES = 4;
+  constexpr int BN = 256, BK = 64;
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
   constexpr int FM = BMT / 64, FN = 4;
-  constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 16384 bf16 = 32 KB
-  constexpr int LA = BMT / 64;                 // A copies (1 KB = 16 rows) per wave per K tile
-  constexpr int LOADS = LA + 4;                // + 4 B copies
-  constexpr int NQ = (FM + FN) * 2;            // fragments per K tile
-  constexpr int NG = FM * FN / 2;              // groups of 4 MFMAs per K tile
+  constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 32768 bf16 = 64 KB
+  constexpr int LA = BMT / 32;                 // A copies (1 KB = 8 rows) per wave per K tile
+  constexpr int LOADS = LA + 8;                // + 8 B copies
+  constexpr int NQ = FM + FN;                  // fragments per 16-wide step
   static_assert(BNO == (SWIGLU ? 128 : 256), "tile");
+  static_assert(LOADS % 4 == 0 && (NQ * 4) % 8 == 0, "schedule");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // loader: copy j < LA covers A rows (wave*LA + j)*16 + lane/4, copy j >= LA
-  // covers B rows (wave*4 + j-LA)*16 + lane/4; the lane's 16 B is logical
-  // chunk (lane & 3) ^ f(row) of that row.
+  // loader: copy j < LA covers A rows (wave*LA + j)*8 + lane/8, copy j >= LA
+  // covers B rows (wave*8 + j-LA)*8 + lane/8; the lane's 16 B is logical
+  // chunk (lane & 7) ^ f(row) of that row.
   const uint16_t* src[LOADS];
 #pragma unroll
   for (int j = 0; j < LOADS; j++) {
     const bool isa = j < LA;
-    const int row = (isa ? (wave * LA + j) : (wave * 4 + j - LA)) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ lds_swz(row);
+    const int row = (isa ? (wave * LA + j) : (wave * 8 + j - LA)) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ lds_swz8(row);
     const uint16_t* p;
     if (isa) {
       p = a_row<uint16_t, SWIGLU>(args, c, row);
@@ -308,9 +323,9 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
     src[j] = p + chunk * 8;
   }
   auto copy_one = [&](int kt, int j) {
-    uint16_t* st = lds + (kt % STAGES) * STAGE_ELEMS;
+    uint16_t* st = lds + (kt & 1) * STAGE_ELEMS;
     const bool isa = j < LA;
-    const int row0 = isa ? (wave * LA + j) * 16 : BM + (wave * 4 + j - LA) * 16;
+    const int row0 = isa ? (wave * LA + j) * 8 : BM + (wave * 8 + j - LA) * 8;
     dl_copy16(src[j] + kt * BK, st + row0 * BK);
   };
 
@@ -333,87 +348,77 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
     }
   }
   const int frow = lane & 31;
-  const int fsw = lds_swz(frow);
+  const int fsw = lds_swz8(frow);
   const int fhalf = lane >> 5;
   const int nk = c.K / BK;
 
-  // fragments of one K tile (two 16-wide MFMA steps), double buffered in
-  // registers: tile kt+1 is read from LDS while tile kt is multiplied.
-  // Fragment q of a tile: step q / (FM+FN), then A (index < FM) or B.
+  // fr[b][q]: fragments of one 16-wide step; q < FM are A, the rest B
   bf16x8 fr[2][NQ];
-  auto read_frag = [&](int kt, int buf, int q) {
-    const uint16_t* st = lds + (kt % STAGES) * STAGE_ELEMS;
-    const int s = q / (FM + FN), i = q % (FM + FN);
+  auto read_frag = [&](int kt, int s, int buf, int q) {
+    const uint16_t* st = lds + (kt & 1) * STAGE_ELEMS;
     const int ch = ((2 * s + fhalf) ^ fsw) * 8;
-    const int row = i < FM ? (wm * FM + i) * 32 + frow : BM + brow[i - FM] + frow;
+    const int row = q < FM ? (wm * FM + q) * 32 + frow : BM + brow[q - FM] + frow;
     fr[buf][q] = *reinterpret_cast<const bf16x8*>(st + row * BK + ch);
   };
-  auto wait_tile = [&](int t, int issued_upto) {
-    const int later = (issued_upto < nk - 1 ? issued_upto : nk - 1) - t;
-    if (later >= 3) wait_vmcnt<3 * LOADS>();
-    else if (later == 2) wait_vmcnt<2 * LOADS>();
-    else if (later == 1) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
+  auto mfma4 = [&](int buf, int g) {  // MFMAs 4g .. 4g+3 of one step
+#pragma unroll
+    for (int m = 4 * g; m < 4 * g + 4; m++) {
+      const int fm = m / FN, fn = m % FN;
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][FM + fn], fr[buf][fm],
+                                                            acc[fm][fn], 0, 0, 0);
+    }
   };
+  constexpr int GPS = FM * FN / 4;   // groups of 4 MFMAs per step
+  constexpr int RPG = (NQ + GPS - 1) / GPS;  // fragment reads per group
+  constexpr int CPG = LOADS / GPS;   // copies per group in step 3
 
-  // prologue: fill all stages, then stage tile 0's fragments
+  // prologue: tiles 0 and 1 in flight, tile 0 published, its step-0
+  // fragments in registers
 #pragma unroll
-  for (int t = 0; t < STAGES; t++)
-    if (t < nk)
+  for (int j = 0; j < LOADS; j++) copy_one(0, j);
+  if (nk > 1)
 #pragma unroll
-      for (int j = 0; j < LOADS; j++) copy_one(t, j);
-  wait_tile(0, STAGES - 1);
+    for (int j = 0; j < LOADS; j++) copy_one(1, j);
+  if (nk > 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int q = 0; q < NQ; q++) read_frag(0, 0, q);
+  for (int q = 0; q < NQ; q++) read_frag(0, 0, 0, q);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
-  // One K tile: make tile kt+1 visible, then NG groups of {copies of tile
-  // kt+STAGES into tile kt's stage, fragment reads of tile kt+1, four MFMAs
-  // of tile kt}, so copy issue and LDS reads are spread over the MFMAs.
-  auto step = [&](int kt, auto buf_c, auto steady_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    constexpr bool steady = decltype(steady_c)::value;  // copies and reads all valid
-    const bool more = steady || kt + 1 < nk;
-    const bool refill = steady || kt + STAGES < nk;
+  for (int kt = 0; kt < nk; kt++) {
+    // steps 0..2: read step s+1 while multiplying step s
+#pragma unroll
+    for (int s = 0; s < 3; s++) {
+#pragma unroll
+      for (int g = 0; g < GPS; g++) {
+#pragma unroll
+        for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(kt, s + 1, (s + 1) & 1, q);
+        mfma4(s & 1, g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    }
+    // step 3: publish tile kt+1, refill tile kt's stage with tile kt+2,
+    // read tile kt+1's step-0 fragments
+    const bool more = kt + 1 < nk;
+    const bool refill = kt + 2 < nk;
     if (more) {
-      // tile kt+1 has landed for every wave, and every wave has finished
-      // reading tile kt from LDS (its reads completed before this barrier)
-      if (steady) wait_vmcnt<(STAGES - 2) * LOADS>();
-      else wait_tile(kt + 1, kt + STAGES - 1);
-      __builtin_amdgcn_s_barrier();
+      wait_vmcnt<0>();                      // this wave's copies of tile kt+1
+      __builtin_amdgcn_s_barrier();         // ... and everyone's; tile kt fully read
     }
 #pragma unroll
-    for (int g = 0; g < NG; g++) {
+    for (int g = 0; g < GPS; g++) {
       if (refill)
 #pragma unroll
-        for (int j = g * LOADS / NG; j < (g + 1) * LOADS / NG; j++) copy_one(kt + STAGES, j);
+        for (int j = g * CPG; j < (g + 1) * CPG; j++) copy_one(kt + 2, j);
       if (more)
 #pragma unroll
-        for (int q = g * NQ / NG; q < (g + 1) * NQ / NG; q++) read_frag(kt + 1, buf ^ 1, q);
-#pragma unroll
-      for (int m = 4 * g; m < 4 * g + 4; m++) {
-        const int s = m / (FM * FN), fm = (m / FN) % FM, fn = m % FN;
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            fr[buf][s * (FM + FN) + FM + fn], fr[buf][s * (FM + FN) + fm], acc[fm][fn], 0, 0, 0);
-      }
+        for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(kt + 1, 0, 0, q);
+      mfma4(1, g);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): next tile's fragments are in registers
-  };
-  // nk is even (K is a multiple of 64): unrolled by two so the register
-  // buffer index is a compile-time constant.  The steady part (every tile
-  // still has a refill) runs without per-group conditions.
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  int kt = 0;
-  for (; kt + STAGES < nk; kt += 2) {
-    step(kt, I0{}, std::true_type{});
-    step(kt + 1, I1{}, std::true_type{});
-  }
-  for (; kt < nk; kt += 2) {
-    step(kt, I0{}, std::false_type{});
-    step(kt + 1, I1{}, std::false_type{});
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
 
   // epilogue.  acc[fm][fn][e] = C[row = (wm*FM + fm)*32 + lane%32]
@@ -468,7 +473,7 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
 // of a 256-row tile instead of most of it.
 template <bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * (256 + 256) * 32];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * (256 + 256) * 64];
   int tile_id, n_tile;
   if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
