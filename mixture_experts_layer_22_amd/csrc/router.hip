@@ -36,72 +36,95 @@ __global__ void k_split_router(const float* __restrict__ W, uint16_t* __restrict
 // Partial logits over a K range:
 //   part[z][t, col_off + n] = x[t, x_off + K_z] . W[n, K_z]   (n < NL)
 // with K_z the z-th of gridDim.z equal K ranges (split K keeps enough
-// waves busy at small T; the selection kernel adds the partials in order z).
+// blocks busy at small T; the selection kernel adds the partials in order z).
 // bf16 x; W given as three bf16 slices W3[p * slice + n * K + kk].
-// Block: 64 tokens x 64 logits, wave w owns logits 16w..16w+15 for all 64
-// tokens (4 v_mfma_f32_16x16x32_bf16 tiles), so every weight fragment is
-// used for 64 tokens.  Operands go straight from global memory to MFMA
-// registers: per 64-wide K block, lane (r = l%16, q = l/16) loads 16
-// consecutive elements of its row at q*16 and MFMA step h uses elements
-// [q*16 + 8h, +8).  A and B share that K permutation, so the dot products
-// are unchanged while every row is read as one 128-byte run.  The three
-// weight slices accumulate into one fp32 accumulator.
+//
+// Block: 64 tokens x 64 logits; wave w owns tokens 16w..16w+15 and all 64
+// logits (four v_mfma_f32_16x16x32_bf16 tiles).  Per 64-wide K chunk the
+// three weight slices of the block's 64 logits (24 KB) are staged in LDS
+// once and shared by the four waves (double buffered); x fragments go
+// straight from global memory to registers.  K is permuted identically for
+// both operands: lane (r = l%16, q = l/16) takes elements [16q, 16q+16) of
+// the chunk, MFMA step h the half [16q + 8h, +8), so each x row is one
+// 128-byte run.  The three slices accumulate into one fp32 accumulator.
+__device__ __forceinline__ int rl_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 __global__ __launch_bounds__(256) void k_router_logits_bf16(
     const uint16_t* __restrict__ x, int64_t T, int ldx, int x_off,
     const uint16_t* __restrict__ W3, int64_t slice, int NL, int K,
     float* __restrict__ logits, int ldl, int col_off, int64_t part_stride) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 64;
-  const int n0 = blockIdx.y * 64 + wave * 16;
-  if (n0 >= NL) return;
+  // [buf][slice * 64 + logit][64 K] bf16, 16-byte chunks swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][3 * 64 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  const int n0 = blockIdx.y * 64;
   const int kc = K / gridDim.z;
-  const int kbeg = blockIdx.z * kc, kend = kbeg + kc;
+  const int kbeg = blockIdx.z * kc, nch = kc / 64;
   const int r = lane & 15, q = lane >> 4;
-  const uint16_t* ap[4];
+  int64_t am = m0 + r;
+  if (am >= T) am = T - 1;  // clamped rows feed only outputs that are not stored
+  const uint16_t* ap = x + am * (int64_t)ldx + x_off + kbeg + q * 16;
+
+  // B loader: 3 * 64 rows x 8 chunks = 1536 chunks, 6 per thread
+  const uint16_t* bsrc[6];
+  int bdst[6];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    int64_t m = m0 + 16 * i + r;
-    if (m >= T) m = T - 1;  // clamped rows feed only outputs that are not stored
-    ap[i] = x + m * (int64_t)ldx + x_off + q * 16;
+  for (int i = 0; i < 6; i++) {
+    const int id = tid + 256 * i;          // 0 .. 1535
+    const int row = id >> 3, ch = id & 7;  // row = slice * 64 + logit
+    const int p = row >> 6, nl = row & 63;
+    const int n = n0 + nl < NL ? n0 + nl : NL - 1;
+    bsrc[i] = W3 + p * slice + (int64_t)n * K + kbeg + ch * 8;
+    bdst[i] = row * 64 + ((ch ^ rl_swz(row)) * 8);
   }
-  const int bn = n0 + r < NL ? n0 + r : NL - 1;
-  const uint16_t* bp = W3 + (int64_t)bn * K + q * 16;
+  u32x4 breg[6];
+  auto bload = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 6; i++) breg[i] = *reinterpret_cast<const u32x4*>(bsrc[i] + c * 64);
+  };
+  auto bstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 6; i++) *reinterpret_cast<u32x4*>(&bs[buf][bdst[i]]) = breg[i];
+  };
+
   f32x4 acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int kb = kbeg; kb < kend; kb += 64) {
-    u32x4 a[4][2], b[3][2];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      a[i][0] = *reinterpret_cast<const u32x4*>(ap[i] + kb);
-      a[i][1] = *reinterpret_cast<const u32x4*>(ap[i] + kb + 8);
-    }
-#pragma unroll
-    for (int p = 0; p < 3; p++) {
-      b[p][0] = *reinterpret_cast<const u32x4*>(bp + p * slice + kb);
-      b[p][1] = *reinterpret_cast<const u32x4*>(bp + p * slice + kb + 8);
-    }
+  for (int j = 0; j < 4; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bload(0);
+  bstore(0);
+  __syncthreads();
+  for (int c = 0; c < nch; c++) {
+    const int buf = c & 1;
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap + c * 64);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + c * 64 + 8);
+    if (c + 1 < nch) bload(c + 1);
 #pragma unroll
     for (int p = 0; p < 3; p++)
 #pragma unroll
-      for (int h = 0; h < 2; h++)
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][h]),
-                                                           __builtin_bit_cast(bf16x8, b[p][h]),
-                                                           acc[i], 0, 0, 0);
+      for (int j = 0; j < 4; j++) {
+        const int row = p * 64 + j * 16 + r;
+        const int sw = rl_swz(row);
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(&bs[buf][row * 64 + (((2 * q) ^ sw) * 8)]);
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(&bs[buf][row * 64 + (((2 * q + 1) ^ sw) * 8)]);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                         __builtin_bit_cast(bf16x8, b0), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                         __builtin_bit_cast(bf16x8, b1), acc[j], 0, 0, 0);
+      }
+    if (c + 1 < nch) bstore(buf ^ 1);
+    __syncthreads();
   }
-  // lane holds C[16 i + 4 q + j][r]
-  const int n = n0 + r;
+  // lane holds C[4 q + e][16 j + r] of its wave's 16 tokens
   float* out = logits + blockIdx.z * part_stride;
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int j = 0; j < 4; j++) {
+    const int n = n0 + 16 * j + r;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t m = m0 + 16 * i + 4 * q + j;
-      if (m < T && n < NL) out[m * ldl + col_off + n] = acc[i][j];
+    for (int e = 0; e < 4; e++) {
+      const int64_t m = m0 + 4 * q + e;
+      if (m < T && n < NL) out[m * ldl + col_off + n] = acc[j][e];
     }
+  }
 }
 
 // fp32 layers: one thread per logit, four interleaved fp32 partial sums.
@@ -299,7 +322,7 @@ int router_splits(int dtype, int64_t T, int NL, int K) {
   if (dtype != MOE_BF16) return 1;
   const int64_t blocks = cdiv(T, 64) * cdiv(NL, 64);
   int S = 1;
-  while (S < 8 && blocks * S < 256 && K % (64 * 2 * S) == 0) S *= 2;
+  while (S < 16 && blocks * S < 512 && K % (64 * 2 * S) == 0) S *= 2;
   return S;
 }
 
