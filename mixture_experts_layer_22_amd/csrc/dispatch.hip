@@ -9,9 +9,10 @@
 // Each pass is a per-tile digit histogram, one exclusive scan over
 // (digit, tile) in digit-major order, and a stable scatter whose in-tile
 // ranks come from wave ballots.  Stability of every pass keeps tasks of one
-// expert in task order, i.e. by token.  Only integer atomics on LDS or
-// per-expert counters are used, and their results do not depend on order,
-// so the output is bit-exact and deterministic.
+// expert in task order, i.e. by token.  Group offsets come from the scan
+// (one pass) or from the segment boundaries of the sorted order (several
+// passes).  The only atomics are integer adds on LDS counters, whose results
+// do not depend on order, so the output is bit-exact and deterministic.
 #include "kernels.h"
 
 namespace moe {
@@ -25,142 +26,44 @@ __global__ void k_fill_i32(int32_t* p, int32_t v, int64_t n) {
   if (i < n) p[i] = v;
 }
 
-// ids outside [0, E) are not counted (they are a caller error; skipping
-// them keeps every access in bounds)
-__global__ void k_count_experts(const int32_t* __restrict__ idx, int64_t n, int E,
-                                int32_t* counts) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) {
-    const int32_t e = idx[i];
-    if ((uint32_t)e < (uint32_t)E) atomicAdd(&counts[e], 1);
-  }
-}
-
-// Exclusive scan of n ints by one block of 1024 threads: out[0] = 0,
-// out[i] = in[0] + ... + in[i-1]; also writes out[n] (the total) when
-// write_total.  in and out may alias.
-__global__ __launch_bounds__(1024) void k_scan_single_block(const int32_t* in, int32_t* out,
-                                                            int64_t n, int write_total) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t lo = tid * per;
-  const int64_t hi = lo + per < n ? lo + per : n;
-  int32_t s = 0;
-  for (int64_t i = lo; i < hi; i++) s += in[i];
-  part[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
-  for (int o = 1; o < 1024; o <<= 1) {
-    int32_t v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int32_t run = tid ? part[tid - 1] : 0;
-  for (int64_t i = lo; i < hi; i++) {
-    int32_t v = in[i];
-    out[i] = run;
-    run += v;
-  }
-  if (write_total && tid == 1023) out[n] = part[1023];
-}
-
-// Multi-block exclusive scan for long arrays: each block of 256 threads
-// covers 4096 consecutive ints (16 per thread, loaded as four 16-byte
-// vectors); pass 1 writes block totals, the totals are scanned by one
-// block, pass 2 rescans each block locally and adds its offset.
-constexpr int kScanThreads = 256;
-constexpr int kScanPer = 16;
-constexpr int kScanTile = kScanThreads * kScanPer;
-
-__device__ __forceinline__ int32_t block_exclusive_sum(int32_t v, int32_t* lds_w, int32_t& total) {
+// Exclusive scan over the 256 threads of a block (4 waves): returns the
+// sum of v over lower threads and sets total.  wsum: 4 ints of LDS.  Ends
+// with a barrier, so wsum can be reused at once.
+__device__ __forceinline__ int32_t block256_exclusive(int32_t v, int32_t* wsum, int32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int32_t inc = v;
+  int32_t x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int32_t t = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += t;
+    const int32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
   }
-  if (lane == 63) lds_w[w] = inc;
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
-  int32_t wbase = 0;
-  total = 0;
+  int32_t pre = 0;
 #pragma unroll
-  for (int i = 0; i < kScanThreads / 64; i++) {
-    const int32_t t = lds_w[i];
-    if (i < w) wbase += t;
-    total += t;
-  }
-  return wbase + inc - v;
+  for (int ww = 0; ww < 4; ww++) pre += ww < w ? wsum[ww] : 0;
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return pre + x - v;
 }
 
-__device__ __forceinline__ void load16(const int32_t* in, int64_t n, int64_t base, int32_t v[16]) {
-  if (base + 16 <= n && ((uintptr_t)(in + base) & 15) == 0) {
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      int4 t = reinterpret_cast<const int4*>(in + base)[q];
-      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; i++) v[i] = base + i < n ? in[base + i] : 0;
+// Multi-pass sorts: block `digit` scans its row hist[digit, 0..nb) of the
+// tile histogram in place (exclusive, tiles in order) and writes the row
+// total; the scatter adds the exclusive scan of the totals over digits.
+__global__ __launch_bounds__(256) void k_digit_scan(int32_t* __restrict__ hist, int nb,
+                                                    int32_t* __restrict__ totals) {
+  __shared__ int32_t wsum[4];
+  int32_t* row = hist + (int64_t)blockIdx.x * nb;
+  int32_t carry = 0;
+  for (int base = 0; base < nb; base += 256) {
+    const int i = base + threadIdx.x;
+    const int32_t v = i < nb ? row[i] : 0;
+    int32_t tot;
+    const int32_t ex = block256_exclusive(v, wsum, tot);
+    if (i < nb) row[i] = carry + ex;
+    carry += tot;
   }
-}
-
-__global__ __launch_bounds__(kScanThreads) void k_scan_totals(const int32_t* __restrict__ in,
-                                                              int64_t n,
-                                                              int32_t* __restrict__ totals) {
-  __shared__ int32_t lds_w[kScanThreads / 64];
-  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kScanPer;
-  int32_t v[16];
-  load16(in, n, base, v);
-  int32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) s += v[i];
-  int32_t total;
-  block_exclusive_sum(s, lds_w, total);
-  if (threadIdx.x == 0) totals[blockIdx.x] = total;
-}
-
-// out may alias in.  offsets: scanned block totals (nullptr: one block).
-__global__ __launch_bounds__(kScanThreads) void k_scan_finish(const int32_t* in, int32_t* out,
-                                                              int64_t n,
-                                                              const int32_t* __restrict__ offsets,
-                                                              int32_t* total_out) {
-  __shared__ int32_t lds_w[kScanThreads / 64];
-  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kScanPer;
-  int32_t v[16];
-  load16(in, n, base, v);
-  int32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) s += v[i];
-  int32_t total;
-  int32_t run = block_exclusive_sum(s, lds_w, total) + (offsets ? offsets[blockIdx.x] : 0);
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    if (base + i < n) out[base + i] = run;
-    run += v[i];
-  }
-  if (total_out && blockIdx.x == gridDim.x - 1 && threadIdx.x == 0)
-    *total_out = (offsets ? offsets[blockIdx.x] : 0) + total;
-}
-
-// exclusive scan of n ints (in may equal out); writes *total_out when given.
-// scratch: cdiv(n, 4096) + 1 ints.
-static void exclusive_scan(const int32_t* in, int32_t* out, int64_t n, int32_t* total_out,
-                           int32_t* scratch, hipStream_t st) {
-  const int64_t nblk = cdiv(n, kScanTile);
-  if (nblk <= 1) {
-    hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kScanThreads), 0, st, in, out, n,
-                       (const int32_t*)nullptr, total_out);
-    return;
-  }
-  hipLaunchKernelGGL(k_scan_totals, dim3((unsigned)nblk), dim3(kScanThreads), 0, st, in, n,
-                     scratch);
-  hipLaunchKernelGGL(k_scan_single_block, dim3(1), dim3(1024), 0, st, scratch, scratch, nblk, 0);
-  hipLaunchKernelGGL(k_scan_finish, dim3((unsigned)nblk), dim3(kScanThreads), 0, st, in, out, n,
-                     (const int32_t*)scratch, total_out);
+  if (threadIdx.x == 0) totals[blockIdx.x] = carry;
 }
 
 // Single-pass dispatch (E <= 256): exclusive scan of the digit-major tile
@@ -201,6 +104,7 @@ __device__ __forceinline__ int radix_digit(const int32_t* idx, int32_t task, int
 }
 
 // Per-tile digit histogram: hist[digit * nb + tile].
+template <int ITEMS>
 __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __restrict__ idx,
                                                               const int32_t* __restrict__ src,
                                                               int64_t n, int shift, int bits,
@@ -210,9 +114,9 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __r
   const int mask = (1 << bits) - 1;
   cnt[tid] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kRadixTile;
+  const int64_t base = (int64_t)blockIdx.x * kRadixThreads * ITEMS;
 #pragma unroll
-  for (int r = 0; r < kRadixItems; r++) {
+  for (int r = 0; r < ITEMS; r++) {
     int64_t i = base + r * kRadixThreads + tid;
     if (i < n) {
       int32_t task = src ? src[i] : (int32_t)i;
@@ -226,22 +130,31 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __r
 // Stable scatter.  Items of a tile are taken in task order r*256 + w*64 + l;
 // an item's destination is base[digit, tile] + (same-digit items earlier in
 // the tile).  Same-digit lanes of a wave are found with one ballot per key
-// bit.  The last pass also writes the inverse permutation.
+// bit.  base[digit, tile] is the scanned histogram, plus the exclusive scan
+// of the digit totals when those are given (multi-pass sorts).  The last
+// pass also writes the inverse permutation.
+template <int ITEMS>
 __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ src, int64_t n, int shift,
-    int bits, const int32_t* __restrict__ hist_scanned, int nb, int32_t* __restrict__ dst,
-    int32_t* __restrict__ inv) {
+    int bits, const int32_t* __restrict__ hist_scanned, const int32_t* __restrict__ digit_totals,
+    int nb, int32_t* __restrict__ dst, int32_t* __restrict__ inv) {
   __shared__ int32_t run[256];
   __shared__ int32_t wcnt[kRadixThreads / 64][256];
+  __shared__ int32_t wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int mask = (1 << bits) - 1;
-  run[tid] = tid <= mask ? hist_scanned[(int64_t)tid * nb + blockIdx.x] : 0;
+  int32_t start = tid <= mask ? hist_scanned[(int64_t)tid * nb + blockIdx.x] : 0;
+  if (digit_totals) {
+    int32_t unused;
+    start += block256_exclusive(tid <= mask ? digit_totals[tid] : 0, wsum, unused);
+  }
+  run[tid] = start;
 #pragma unroll
   for (int ww = 0; ww < kRadixThreads / 64; ww++) wcnt[ww][tid] = 0;
   __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t base = (int64_t)blockIdx.x * kRadixTile;
-  for (int r = 0; r < kRadixItems; r++) {
+  const int64_t base = (int64_t)blockIdx.x * kRadixThreads * ITEMS;
+  for (int r = 0; r < ITEMS; r++) {
     const int64_t i = base + r * kRadixThreads + tid;
     const bool valid = i < n;
     int32_t task = 0;
@@ -276,17 +189,42 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
   }
 }
 
+// offsets[e] = first sorted position whose expert is >= e, read off the
+// sorted order: position p writes every e in (key(p-1), key(p)] (key(-1) =
+// -1, key(n) = E), so each of offsets[0..E] is written exactly once.  The key
+// is the id's low `bits` bits -- what the passes sorted on -- clamped to E,
+// which keeps it non-decreasing along the order even for ids outside [0, E)
+// (a caller error: such tasks end up past offsets[E], in no expert's group).
+__global__ void k_segment_offsets(const int32_t* __restrict__ idx, const int32_t* __restrict__ perm,
+                                  int64_t n, int E, int bits, int32_t* __restrict__ offsets) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p > n) return;
+  const int32_t mask = (int32_t)((1u << bits) - 1);
+  auto key = [&](int64_t q) {
+    const int32_t e = idx[perm[q]] & mask;
+    return e > E ? E : e;
+  };
+  const int lo = p > 0 ? key(p - 1) : -1;
+  const int hi = p < n ? key(p) : E;
+  for (int e = lo + 1; e <= hi; e++) offsets[e] = (int32_t)p;
+}
+
+__global__ void k_counts_from_offsets(const int32_t* __restrict__ offsets, int E,
+                                      int32_t* __restrict__ counts) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) counts[e] = offsets[e + 1] - offsets[e];
+}
+
 // ------------------------------------------------------------------------
 
 int64_t dispatch_scratch_ints(int64_t n, int E) {
-  int bits = 0;
-  while ((1ll << bits) < E) bits++;
-  int passes = bits ? (bits + 7) / 8 : 1;
-  int64_t nb = cdiv(n, kRadixTile);
-  // hist (256 * nb) + for multi-pass sorts one temp array of n and the
-  // scan's block totals
-  const int64_t scan = cdiv((256 * nb > E ? 256 * nb : E), kScanTile) + 1;
-  return 256 * nb + (passes > 1 ? n + scan : 0);
+  int passes = 0;
+  while ((1ll << (8 * passes)) < E) passes++;
+  if (passes == 0) passes = 1;
+  const int64_t nb = cdiv(n, kRadixTile);
+  // hist (256 * nb); multi-pass sorts add the digit totals and one temp
+  // array of n
+  return 256 * nb + (passes > 1 ? 256 + n : 0);
 }
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
@@ -295,9 +233,6 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
   int bits = 0;
   while ((1ll << bits) < E) bits++;
   if (bits == 0) bits = 1;  // one expert: a pass on a constant digit keeps task order
-  const int nb = (int)cdiv(n, kRadixTile);
-  int32_t* hist = scratch;
-  int32_t* tmp = scratch + 256 * (int64_t)nb;
   if (n == 0) {
     hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)cdiv(E, 256)), dim3(256), 0, st, counts, 0,
                        (int64_t)E);
@@ -307,22 +242,23 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
   }
   if (bits <= 8) {
     // one pass: histogram, scan (+ counts and offsets), stable scatter
-    hipLaunchKernelGGL(k_radix_hist, dim3(nb), dim3(kRadixThreads), 0, st, idx,
+    const int nb = (int)cdiv(n, kRadixTile);
+    int32_t* hist = scratch;
+    hipLaunchKernelGGL(k_radix_hist<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
                        (const int32_t*)nullptr, n, 0, bits, hist, nb);
     hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, st, hist,
                        (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets);
-    hipLaunchKernelGGL(k_radix_scatter, dim3(nb), dim3(kRadixThreads), 0, st, idx,
-                       (const int32_t*)nullptr, n, 0, bits, hist, nb, perm, inv_perm);
+    hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
+                       (const int32_t*)nullptr, n, 0, bits, hist, (const int32_t*)nullptr, nb,
+                       perm, inv_perm);
     return hipGetLastError();
   }
-  // many experts: per-expert counts by atomics on global counters (spread
-  // over many bins), then 8-bit LSD passes
-  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)cdiv(E, 256)), dim3(256), 0, st, counts, 0,
-                     (int64_t)E);
-  hipLaunchKernelGGL(k_count_experts, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, idx, n, E,
-                     counts);
-  int32_t* scan_scratch = tmp + n;
-  exclusive_scan(counts, offsets, (int64_t)E, offsets + E, scan_scratch, st);
+  // many experts: 8-bit LSD passes (hist, per-digit scan, scatter), then
+  // offsets and counts read off the sorted order
+  const int nb = (int)cdiv(n, kRadixTile);
+  int32_t* hist = scratch;
+  int32_t* totals = scratch + 256 * (int64_t)nb;
+  int32_t* tmp = totals + 256;
   const int passes = (bits + 7) / 8;
   const int32_t* src = nullptr;
   for (int p = 0; p < passes; p++) {
@@ -331,13 +267,18 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     const bool last = p == passes - 1;
     // ping-pong so that the last pass lands in perm
     int32_t* dst = ((passes - 1 - p) % 2) ? tmp : perm;
-    hipLaunchKernelGGL(k_radix_hist, dim3(nb), dim3(kRadixThreads), 0, st, idx, src, n, shift,
-                       pb, hist, nb);
-    exclusive_scan(hist, hist, (int64_t)(1 << pb) * nb, (int32_t*)nullptr, scan_scratch, st);
-    hipLaunchKernelGGL(k_radix_scatter, dim3(nb), dim3(kRadixThreads), 0, st, idx, src, n, shift,
-                       pb, hist, nb, dst, last ? inv_perm : (int32_t*)nullptr);
+    hipLaunchKernelGGL(k_radix_hist<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx, src,
+                       n, shift, pb, hist, nb);
+    hipLaunchKernelGGL(k_digit_scan, dim3(1u << pb), dim3(256), 0, st, hist, nb, totals);
+    hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
+                       src, n, shift, pb, hist, (const int32_t*)totals, nb, dst,
+                       last ? inv_perm : (int32_t*)nullptr);
     src = dst;
   }
+  hipLaunchKernelGGL(k_segment_offsets, dim3((unsigned)cdiv(n + 1, 256)), dim3(256), 0, st, idx,
+                     perm, n, E, bits, offsets);
+  hipLaunchKernelGGL(k_counts_from_offsets, dim3((unsigned)cdiv(E, 256)), dim3(256), 0, st,
+                     offsets, E, counts);
   return hipGetLastError();
 }
 
