@@ -238,18 +238,24 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
 }
 
 // ------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM, 256 x 256 (B rows) tiles, direct-to-LDS pipeline.
+// bf16 MFMA grouped GEMM, BMT x 256 (B rows) tiles, direct-to-LDS pipeline.
 //
 // Global -> LDS copies use global_load_lds_dwordx4 (no staging registers):
-// lane i of a wave lands 16 bytes at LDS base + 16 i.  K is cut into 32-wide
-// tiles; four LDS stages of 32 KB (A 256 x 32 + B 256 x 32 bf16) keep three
-// tiles in flight while the fourth is multiplied, so HBM/L2 latency hides
-// behind about 3000 cycles of MFMA work.  One barrier per K tile.
+// lane i of a wave lands 16 bytes at LDS base + 16 i.  K advances in 32-wide
+// tiles held in a ring of five LDS stages of 32 KB (A rows [0, 256), B rows
+// [256, 512), 64 B per row), i.e. all 160 KB of the CU's LDS.  A K tile is
+// two 16-wide MFMA steps; the fragments of the next step are read while the
+// current one multiplies (double buffered in registers).
 //
-// LDS rows are 64 bytes (4 chunks of 16 B); chunk c of row r sits at
-// c ^ f(r), f(r) = ((r >> 1) & 3) ^ ((r >> 2) & 3).  An MFMA fragment read
-// (32 consecutive rows, one chunk) then touches distinct banks within every
-// 8 lanes (32 x 4-byte banks) and within every 16 lanes (64 banks).
+// One barrier per K tile, between its two steps: it publishes tile t+1 (each
+// wave first waits for its own copies) and certifies that every wave holds
+// tile t's last fragments, so tile t's stage can take tile t+5.  A copy is
+// issued three to four K tiles (six to eight steps) before it is needed.
+//
+// LDS rows are 4 chunks of 16 B; chunk c of row r sits at c ^ f(r),
+// f(r) = ((r >> 1) & 3) ^ ((r >> 2) & 3).  An MFMA fragment read (32
+// consecutive rows, one chunk) then touches distinct banks within every 8
+// lanes (32 x 4-byte banks) and within every 16 lanes (64 banks).
 //
 // Rows past the group's end (A) or past N (B) are pointed at a valid row:
 // their products only reach output rows / columns that are not stored.
@@ -269,69 +275,131 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// One tile of BMT (256 or 128) rows x 256 B rows.  Waves form a 2 x 2
-// grid; a wave owns BMT/2 rows and 128 B rows (FM x 4 fragments of 32x32).
-//
-// K advances in 64-wide tiles held in two LDS stages of 64 KB (A rows
-// [0, 256), B rows [256, 512), 128 B per row).  A K tile is four 16-wide
-// MFMA steps.  Fragments of step s+1 are read while step s multiplies
-// (double buffered in registers).  Between steps 2 and 3 one barrier both
-// publishes tile kt+1 (its copies were issued a whole tile earlier) and
-// frees tile kt's stage, which the copies of tile kt+2 refill during step 3;
-// step 3 also reads tile kt+1's first fragments.  One barrier per 64 MFMAs.
-//
-// LDS rows are 8 chunks of 16 B; chunk c of row r sits at c ^ f(r) with
-// f(r) = (r & 7) ^ ((r >> 3) & 1): a fragment read (32 consecutive rows,
-// one chunk) hits distinct banks within every 8 lanes (32 banks) and every
-// 16 lanes (64 banks).
-__device__ __forceinline__ int lds_swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// vmcnt(n * L) for a wave-uniform n in [0, 4]
+template <int L>
+__device__ __forceinline__ void wait_vmcnt_tiles(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<L>(); break;
+    case 2: wait_vmcnt<2 * L>(); break;
+    case 3: wait_vmcnt<3 * L>(); break;
+    default: wait_vmcnt<4 * L>(); break;
+  }
+}
 
+constexpr int kGemmStages = 5;
+constexpr int kGemmStageElems = 512 * 32;  // 32 KB
+
+// Epilogue.  acc[fm][fn][e] = C[row = (wm*FM + fm)*32 + lane%32]
+//                               [col = fn*32 + 8(e/4) + 4(lane/32) + e%4]
+// (col relative to the wave's first column).  The bf16 tile (BMT x BNO, at
+// most 128 KB) is staged in the idle K stages, then written out as whole
+// rows with 16-byte stores.  In LDS a row is BNO/4 slots of 8 bytes (4
+// columns); slot s of row r sits at s ^ (r & 31), so the 32 rows of a
+// fragment land in distinct banks.
+template <int BMT, bool SWIGLU, int FM, int FN>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const TileCtx<SWIGLU>& c,
+                                              int n0, uint16_t* lds, const f32x16 (&acc)[FM][FN],
+                                              int wm, int wn) {
+  constexpr int BNO = SWIGLU ? 128 : 256;
+  constexpr int SLOTS = BNO / 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int frow = lane & 31, fhalf = lane >> 5;
+  uint2* s8 = reinterpret_cast<uint2*>(lds);
+  __syncthreads();  // every wave is past its last fragment read
+#pragma unroll
+  for (int fm = 0; fm < FM; fm++) {
+    const int row = (wm * FM + fm) * 32 + frow;
+    uint2* srow = s8 + row * SLOTS;
+    if (SWIGLU) {
+#pragma unroll
+      for (int fn = 0; fn < 2; fn++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const int slot = ((wn * 2 + fn) * 32 + 8 * g + 4 * fhalf) / 4;
+          float h[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const float gt = acc[fm][fn][4 * g + e], up = acc[fm][fn + 2][4 * g + e];
+            h[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          }
+          srow[slot ^ frow] = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+        }
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const int slot = ((wn * FN + fn) * 32 + 8 * g + 4 * fhalf) / 4;
+          srow[slot ^ frow] = make_uint2(pack_bf16x2(acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1]),
+                                         pack_bf16x2(acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]));
+        }
+    }
+  }
+  __syncthreads();
+  // 16-byte chunk j of row r is slots 2j, 2j+1: one aligned 16-byte read at
+  // slot 2j ^ (r & 30), halves swapped when r is odd
+  constexpr int CPR = BNO / 8;
+  const int nrows = c.nr < BMT ? c.nr : BMT;
+  const bool full_cols = n0 + BNO <= c.N;
+#pragma unroll 4
+  for (int i = tid; i < nrows * CPR; i += 256) {
+    const int r = i / CPR, j = i - (i / CPR) * CPR;
+    const int col = n0 + 8 * j;
+    if (!full_cols && col >= c.N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(s8 + r * SLOTS + ((2 * j) ^ (r & 30)));
+    const uint4 w = (r & 1) ? make_uint4(v.z, v.w, v.x, v.y) : v;
+    *reinterpret_cast<uint4*>(c_row<uint16_t, SWIGLU>(args, c, r) + col) = w;
+  }
+}
+
+// One tile of BMT (64, 128, 192 or 256) rows x 256 B rows.  Waves form a 2 x 2 grid;
+// a wave owns BMT/2 rows and 128 B rows (FM x 4 fragments of 32x32).
 template <int BMT, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx<SWIGLU>& c,
                                              int n0, uint16_t* lds) {
-  constexpr int BM = 256;                      // LDS layout: A rows [0, 256), B rows after
-  constexpr int BN = 256, BK = 64;
-  constexpr int BNO = SWIGLU ? BN / 2 : BN;
+  constexpr int BN = 256, BK = 32, NS = kGemmStages;
+  constexpr int STAGE = kGemmStageElems;
   constexpr int FM = BMT / 64, FN = 4;
-  constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 32768 bf16 = 64 KB
-  constexpr int LA = BMT / 32;                 // A copies (1 KB = 8 rows) per wave per K tile
-  constexpr int LOADS = LA + 8;                // + 8 B copies
-  constexpr int NQ = FM + FN;                  // fragments per 16-wide step
-  static_assert(BNO == (SWIGLU ? 128 : 256), "tile");
-  static_assert(LOADS % 4 == 0 && (NQ * 4) % 8 == 0, "schedule");
+  constexpr int LA = BMT / 64;               // A copies (16 rows x 64 B) per wave per K tile
+  constexpr int L = LA + 4;                  // + 4 B copies
+  constexpr int NQ = FM + FN;                // fragments per step
+  constexpr int GPS = FM * FN / 4;           // groups of 4 MFMAs per step
+  constexpr int RPG = (NQ + GPS - 1) / GPS;  // fragment reads per group
+  static_assert(4 * L < 64, "vmcnt range");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // loader: copy j < LA covers A rows (wave*LA + j)*8 + lane/8, copy j >= LA
-  // covers B rows (wave*8 + j-LA)*8 + lane/8; the lane's 16 B is logical
-  // chunk (lane & 7) ^ f(row) of that row.
-  const uint16_t* src[LOADS];
+  // loader: copy j < LA covers A rows (wave*LA + j)*16 + lane/4, copy j >= LA
+  // covers B rows 256 + (wave*4 + j-LA)*16 + lane/4; the lane's 16 B is
+  // logical chunk (lane & 3) ^ f(row) of that row's 64-byte K slice.
+  const uint16_t* src[L];
 #pragma unroll
-  for (int j = 0; j < LOADS; j++) {
+  for (int j = 0; j < L; j++) {
     const bool isa = j < LA;
-    const int row = (isa ? (wave * LA + j) : (wave * 8 + j - LA)) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ lds_swz8(row);
+    const int r = (isa ? (wave * LA + j) : (wave * 4 + j - LA)) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ lds_swz(r);
     const uint16_t* p;
     if (isa) {
-      p = a_row<uint16_t, SWIGLU>(args, c, row);
+      p = a_row<uint16_t, SWIGLU>(args, c, r);
       if (!p) p = a_row<uint16_t, SWIGLU>(args, c, 0);
     } else {
-      p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, row);
-      if (!p) p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, SWIGLU && row >= BN / 2 ? BN / 2 : 0);
+      p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, r);
+      if (!p) p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, SWIGLU && r >= BN / 2 ? BN / 2 : 0);
     }
     src[j] = p + chunk * 8;
   }
-  auto copy_one = [&](int kt, int j) {
-    uint16_t* st = lds + (kt & 1) * STAGE_ELEMS;
+  auto copy_one = [&](int t, int stage, int j) {
     const bool isa = j < LA;
-    const int row0 = isa ? (wave * LA + j) * 8 : BM + (wave * 8 + j - LA) * 8;
-    dl_copy16(src[j] + kt * BK, st + row0 * BK);
+    const int row0 = isa ? (wave * LA + j) * 16 : 256 + (wave * 4 + j - LA) * 16;
+    dl_copy16(src[j] + t * BK, lds + stage * STAGE + row0 * BK);
   };
 
   // Accumulators hold C^T fragments: the weight fragment is the MFMA's first
   // operand, so lane l ends up with 4 consecutive output columns of one
-  // output row per 4-element group (stored as one 8-byte write).
+  // output row per 4-element group.
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; i++)
@@ -348,17 +416,15 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
     }
   }
   const int frow = lane & 31;
-  const int fsw = lds_swz8(frow);
+  const int fsw = lds_swz(frow);
   const int fhalf = lane >> 5;
   const int nk = c.K / BK;
 
-  // fr[b][q]: fragments of one 16-wide step; q < FM are A, the rest B
   bf16x8 fr[2][NQ];
-  auto read_frag = [&](int kt, int s, int buf, int q) {
-    const uint16_t* st = lds + (kt & 1) * STAGE_ELEMS;
+  auto read_frag = [&](int stage, int s, int buf, int q) {
     const int ch = ((2 * s + fhalf) ^ fsw) * 8;
-    const int row = q < FM ? (wm * FM + q) * 32 + frow : BM + brow[q - FM] + frow;
-    fr[buf][q] = *reinterpret_cast<const bf16x8*>(st + row * BK + ch);
+    const int row = q < FM ? (wm * FM + q) * 32 + frow : 256 + brow[q - FM] + frow;
+    fr[buf][q] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + ch);
   };
   auto mfma4 = [&](int buf, int g) {  // MFMAs 4g .. 4g+3 of one step
 #pragma unroll
@@ -368,121 +434,113 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
                                                             acc[fm][fn], 0, 0, 0);
     }
   };
-  constexpr int GPS = FM * FN / 4;   // groups of 4 MFMAs per step
-  constexpr int RPG = (NQ + GPS - 1) / GPS;  // fragment reads per group
-  constexpr int CPG = LOADS / GPS;   // copies per group in step 3
+  // The copies of a K tile go out in two halves, spread one or two per
+  // group of 4 MFMAs: copies [0, H) of tile t+5 in step 1 of tile t
+  // (right after the barrier frees tile t's stage) and copies [H, L) in
+  // step 0 of tile t+1.  A steady trickle keeps the memory pipeline from
+  // backing up into the MFMA issue.
+  constexpr int H = (L + 1) / 2;
+  constexpr int CPG = (H + GPS - 1) / GPS;  // copies per group
 
-  // prologue: tiles 0 and 1 in flight, tile 0 published, its step-0
-  // fragments in registers
+  // step 0 of the tile in `stage`: read its step-1 fragments while
+  // multiplying; optionally issue the second half of tile ct's copies
+  auto step0 = [&](int stage, bool copy, int ct, int cst) {
 #pragma unroll
-  for (int j = 0; j < LOADS; j++) copy_one(0, j);
-  if (nk > 1)
+    for (int g = 0; g < GPS; g++) {
+      if (copy)
 #pragma unroll
-    for (int j = 0; j < LOADS; j++) copy_one(1, j);
-  if (nk > 1) wait_vmcnt<LOADS>();
-  else wait_vmcnt<0>();
+        for (int j = H + g * CPG; j < H + (g + 1) * CPG && j < L; j++) copy_one(ct, cst, j);
+#pragma unroll
+      for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(stage, 1, 1, q);
+      mfma4(0, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  };
+
+  // prologue: tiles 0..3 and the first half of tile 4 in flight (one tile
+  // per stage), tile 0 published, its step-0 fragments in registers
+  const int pro = nk < NS - 1 ? nk : NS - 1;
+  for (int t = 0; t < pro; t++)
+#pragma unroll
+    for (int j = 0; j < L; j++) copy_one(t, t, j);
+  if (nk >= NS) {
+#pragma unroll
+    for (int j = 0; j < H; j++) copy_one(NS - 1, NS - 1, j);
+    wait_vmcnt<3 * L + H>();
+  } else {
+    wait_vmcnt_tiles<L>(nk - 1);
+  }
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int q = 0; q < NQ; q++) read_frag(0, 0, 0, q);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
-  for (int kt = 0; kt < nk; kt++) {
-    // steps 0..2: read step s+1 while multiplying step s
-#pragma unroll
-    for (int s = 0; s < 3; s++) {
-#pragma unroll
-      for (int g = 0; g < GPS; g++) {
-#pragma unroll
-        for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(kt, s + 1, (s + 1) & 1, q);
-        mfma4(s & 1, g);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    }
-    // step 3: publish tile kt+1, refill tile kt's stage with tile kt+2,
-    // read tile kt+1's step-0 fragments
-    const bool more = kt + 1 < nk;
-    const bool refill = kt + 2 < nk;
-    if (more) {
-      wait_vmcnt<0>();                      // this wave's copies of tile kt+1
-      __builtin_amdgcn_s_barrier();         // ... and everyone's; tile kt fully read
-    }
+  int st = 0;  // stage of tile t
+  int t = 0;
+  // steady state: tiles t+4 and t+5 exist
+  for (; t + NS < nk; t++) {
+    const int st1 = st == NS - 1 ? 0 : st + 1;
+    const int stp = st == 0 ? NS - 1 : st - 1;  // stage of tile t-1 = tile t+4
+    step0(st, true, t + NS - 1, stp);
+    wait_vmcnt<(NS - 2) * L>();    // this wave's copies of tile t+1 ...
+    __builtin_amdgcn_s_barrier();  // ... and everyone's; tile t fully read
 #pragma unroll
     for (int g = 0; g < GPS; g++) {
-      if (refill)
 #pragma unroll
-        for (int j = g * CPG; j < (g + 1) * CPG; j++) copy_one(kt + 2, j);
-      if (more)
+      for (int j = g * CPG; j < (g + 1) * CPG && j < H; j++) copy_one(t + NS, st, j);
 #pragma unroll
-        for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(kt + 1, 0, 0, q);
+      for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(st1, 0, 0, q);
       mfma4(1, g);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    st = st1;
+  }
+  // drain: at most the second half of the last tile is left to issue
+  for (; t < nk; t++) {
+    const int st1 = st == NS - 1 ? 0 : st + 1;
+    const int stp = st == 0 ? NS - 1 : st - 1;
+    step0(st, t + NS - 1 < nk, t + NS - 1, stp);
+    const bool more = t + 1 < nk;
+    if (more) {
+      wait_vmcnt_tiles<L>(nk - 2 - t);
+      __builtin_amdgcn_s_barrier();
+    }
+#pragma unroll
+    for (int g = 0; g < GPS; g++) {
+      if (more)
+#pragma unroll
+        for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(st1, 0, 0, q);
+      mfma4(1, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    st = st1;
   }
 
-  // epilogue.  acc[fm][fn][e] = C[row = (wm*FM + fm)*32 + lane%32]
-  //                              [col = fn*32 + 8(e/4) + 4(lane/32) + e%4]
-  // (col relative to the wave's first column).  Full tiles skip the bounds
-  // checks; every store writes 4 consecutive bf16 columns.
-  const bool full_rows = c.nr >= BMT;
-  const bool full_cols = n0 + BNO <= c.N;
-#pragma unroll
-  for (int fm = 0; fm < FM; fm++) {
-    const int row = (wm * FM + fm) * 32 + frow;
-    if (!full_rows && row >= c.nr) continue;
-    uint16_t* out = c_row<uint16_t, SWIGLU>(args, c, row);
-    if (SWIGLU) {
-#pragma unroll
-      for (int fn = 0; fn < 2; fn++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const int col = n0 + (wn * 2 + fn) * 32 + 8 * g + 4 * fhalf;
-          float h[4];
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const float gt = acc[fm][fn][4 * g + e], up = acc[fm][fn + 2][4 * g + e];
-            h[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
-          }
-          if (full_cols || col < c.N) {
-            uint2 v;
-            v.x = pack_bf16x2(h[0], h[1]);
-            v.y = pack_bf16x2(h[2], h[3]);
-            *reinterpret_cast<uint2*>(out + col) = v;
-          }
-        }
-    } else {
-#pragma unroll
-      for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const int col = n0 + (wn * FN + fn) * 32 + 8 * g + 4 * fhalf;
-          if (full_cols || col < c.N) {
-            uint2 v;
-            v.x = pack_bf16x2(acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1]);
-            v.y = pack_bf16x2(acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]);
-            *reinterpret_cast<uint2*>(out + col) = v;
-          }
-        }
-    }
-  }
+  gemm_epilogue<BMT, SWIGLU, FM, FN>(args, c, n0, lds, acc, wm, wn);
 }
 
-// A tile of at most 128 valid rows runs the half-height variant, so groups
-// with few tokens (the long tail of expert loads) waste half the MFMA work
-// of a 256-row tile instead of most of it.
+// A tile runs the variant of 64, 128, 192 or 256 rows that covers its valid
+// rows, so the last tile of a group (and the small groups of the long tail
+// of expert loads) wastes at most 63 rows of MFMA work.
 template <bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * (256 + 256) * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kGemmStages * kGemmStageElems];
   int tile_id, n_tile;
   if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
   const int n0 = n_tile * (SWIGLU ? 128 : 256);
   if (n0 >= c.N) return;
-  if (c.nr > 128)
+  if (c.nr > 192)
     gemm_tile_dl<256, SWIGLU>(args, c, n0, lds);
-  else
+  else if (c.nr > 128)
+    gemm_tile_dl<192, SWIGLU>(args, c, n0, lds);
+  else if (c.nr > 64)
     gemm_tile_dl<128, SWIGLU>(args, c, n0, lds);
+  else
+    gemm_tile_dl<64, SWIGLU>(args, c, n0, lds);
 }
 
 // ------------------------------------------------------------------------

@@ -184,6 +184,16 @@ def test_single_expert():
     _forward_vs_oracle(cfg, I.make_inputs(cfg))
 
 
+def test_short_k_big_groups():
+    """256-row tile path with K shorter than the copy pipeline is deep: d = 128
+    (4 K tiles of 32) into the gated GEMM, f = 64 (2 K tiles) into the down
+    projection; groups of ~450 rows take the 256- and 192-row variants."""
+    cfg = I.small_variant("deepseek16b").replace(T=900, d=128, E=4, E_ffn=4, k=2, f=64,
+                                                 n_shared=1, f_shared=64, zipf_s=None)
+    say("short K, big groups")
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
 @pytest.mark.parametrize("tau", [1.0, 0.1])
 def test_moepp_tau(tau):
     cfg = I.small_variant("moepp").replace(tau=tau, T=400)
