@@ -96,7 +96,7 @@ Layout make_layout(const moe_dims* d, int64_t T) {
   L.logits = take((size_t)L.splits * T * L.NL * 4);
   L.disp = take((size_t)dispatch_scratch_ints(L.n, d->E) * 4);
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
-  L.ntiles = take(4);
+  L.ntiles = take(kSchedInts * 4);
   L.h = take(is_pk(d) ? 0 : (size_t)L.n * d->f * es);
   L.hs = take((size_t)d->n_shared * T * d->f_shared * es);
   L.idx = take((size_t)L.n * 4);
@@ -185,7 +185,11 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   const bool gemms = E_groups > 0 || d->n_shared > 0;
   int4* tiles = at<int4*>(ws, L.tiles);
   int32_t* ntiles = at<int32_t*>(ws, L.ntiles);
-  if (gemms) MOE_TRY(launch_build_tiles(offsets, E_groups, d->n_shared, T, L.BM, tiles, ntiles, st));
+  const int N1 = E_groups ? d->f : d->f_shared;
+  const int nn1 = gemm_n_ntiles(d->dtype, true, d->n_shared && d->f_shared > N1 ? d->f_shared : N1);
+  const int nn2 = gemm_n_ntiles(d->dtype, false, d->d);
+  if (gemms)
+    MOE_TRY(launch_build_tiles(offsets, E_groups, d->n_shared, T, L.BM, nn1, nn2, tiles, ntiles, st));
   MOE_TRY(mark(3));
   if (is_pk(d)) {
     MOE_TRY(launch_atomic_h(d->dtype, x, w->atom_u, idx, perm, L.n, d->k, d->d, (float*)y, st));
@@ -196,6 +200,7 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   memset(&g1, 0, sizeof(g1));
   g1.tiles = tiles;
   g1.ntiles = ntiles;
+  g1.xcd_first = ntiles + 1;
   g1.E_ffn = E_groups;
   g1.T = T;
   g1.a_x = x;
@@ -214,6 +219,7 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   if (gemms) MOE_TRY(launch_grouped_gemm(d->dtype, true, L.BM, g1, L.max_tiles, st));
   MOE_TRY(mark(4));
   GemmArgs g2 = g1;
+  g2.xcd_first = ntiles + 1 + (kXcds + 1);
   g2.a_x = nullptr;
   g2.perm = nullptr;
   g2.a_routed = H;

@@ -85,21 +85,20 @@ __device__ __forceinline__ T* c_row(const GemmArgs& a, const TileCtx<SWIGLU>& c,
 }
 
 // ------------------------------------------------------------------------
-// Block -> (M tile, N tile).  Workgroups are handed to the 8 XCDs round-robin
-// (block b runs on XCD b % 8), and each XCD has its own L2.  The W =
-// ntiles * n_ntiles work items are listed M-tile major (the N tiles of one
-// M tile are consecutive: they share the gathered A rows; consecutive M tiles
-// of one expert share its weights) and cut into 8 contiguous chunks, chunk x
-// going to the blocks of XCD x in order.  Blocks past the real work exit.
-__device__ __forceinline__ bool work_item(int ntiles, int n_ntiles, int& m_tile, int& n_tile) {
-  const int W = ntiles * n_ntiles;
+// Block -> (M tile, N tile).  Workgroups go to the 8 XCDs round-robin
+// (block b runs on XCD b % 8, and each XCD runs its blocks in order), and
+// each XCD has its own L2.  The work items are listed M-tile major (the N
+// tiles of one M tile are consecutive: they share the gathered A rows;
+// consecutive M tiles of one expert share its weights) and cut into 8
+// contiguous ranges of about equal cost, range x going to the blocks of XCD
+// x in order.  Blocks past their XCD's range exit.
+__device__ __forceinline__ bool work_item(const GemmArgs& a, int& m_tile, int& n_tile) {
   const int b = blockIdx.x;
-  const int chunk = (W + 7) / 8;
-  const int slot = b / 8;
-  const int w = (b % 8) * chunk + slot;
-  if (slot >= chunk || w >= W) return false;
-  m_tile = w / n_ntiles;
-  n_tile = w - m_tile * n_ntiles;
+  const int x = b % kXcds;
+  const int w = a.xcd_first[x] + b / kXcds;
+  if (w >= a.xcd_first[x + 1]) return false;
+  m_tile = w / a.n_ntiles;
+  n_tile = w - m_tile * a.n_ntiles;
   return true;
 }
 
@@ -121,7 +120,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * BK];
 
   int tile_id, n_tile;
-  if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
+  if (!work_item(args, tile_id, n_tile)) return;
   const int4 tl = args.tiles[tile_id];
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl);
   const int n0 = n_tile * BNO;
@@ -287,8 +286,7 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int n) {
   }
 }
 
-constexpr int kGemmStages = 5;
-constexpr int kGemmStageElems = 512 * 32;  // 32 KB
+constexpr int kGemmLdsElems = 81920;  // 160 KB: all of the CU's LDS
 
 // Epilogue.  acc[fm][fn][e] = C[row = (wm*FM + fm)*32 + lane%32]
 //                               [col = fn*32 + 8(e/4) + 4(lane/32) + e%4]
@@ -303,6 +301,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const TileCt
                                               int wm, int wn) {
   constexpr int BNO = SWIGLU ? 128 : 256;
   constexpr int SLOTS = BNO / 4;
+  constexpr int CPR = BNO / 8;
+  static_assert(BMT * BNO <= kGemmLdsElems, "epilogue staging");
   const int tid = threadIdx.x, lane = tid & 63;
   const int frow = lane & 31, fhalf = lane >> 5;
   uint2* s8 = reinterpret_cast<uint2*>(lds);
@@ -339,7 +339,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const TileCt
   __syncthreads();
   // 16-byte chunk j of row r is slots 2j, 2j+1: one aligned 16-byte read at
   // slot 2j ^ (r & 30), halves swapped when r is odd
-  constexpr int CPR = BNO / 8;
   const int nrows = c.nr < BMT ? c.nr : BMT;
   const bool full_cols = n0 + BNO <= c.N;
 #pragma unroll 4
@@ -353,19 +352,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const TileCt
   }
 }
 
-// One tile of BMT (64, 128, 192 or 256) rows x 256 B rows.  Waves form a 2 x 2 grid;
-// a wave owns BMT/2 rows and 128 B rows (FM x 4 fragments of 32x32).
+// One tile of BMT (64, 128, 192 or 256) rows x 256 B rows.  Waves form a
+// 2 x 2 grid; a wave owns BMT/2 rows and 128 B rows (FM x 4 fragments of
+// 32x32, i.e. up to all 256 AGPRs of accumulators).
 template <int BMT, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx<SWIGLU>& c,
                                              int n0, uint16_t* lds) {
-  constexpr int BN = 256, BK = 32, NS = kGemmStages;
-  constexpr int STAGE = kGemmStageElems;
+  constexpr int BN = 256, BK = 32;
+  constexpr int RA = 256;                    // LDS rows of A; B rows follow
+  constexpr int NS = 5;                      // stages in the ring
+  constexpr int STAGE = (RA + BN) * BK;
+  static_assert(NS * STAGE <= kGemmLdsElems && BMT % 64 == 0 && BMT <= RA, "LDS ring");
   constexpr int FM = BMT / 64, FN = 4;
   constexpr int LA = BMT / 64;               // A copies (16 rows x 64 B) per wave per K tile
   constexpr int L = LA + 4;                  // + 4 B copies
-  constexpr int NQ = FM + FN;                // fragments per step
-  constexpr int GPS = FM * FN / 4;           // groups of 4 MFMAs per step
-  constexpr int RPG = (NQ + GPS - 1) / GPS;  // fragment reads per group
   static_assert(4 * L < 64, "vmcnt range");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -373,7 +373,7 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
   const int wm = wave >> 1, wn = wave & 1;
 
   // loader: copy j < LA covers A rows (wave*LA + j)*16 + lane/4, copy j >= LA
-  // covers B rows 256 + (wave*4 + j-LA)*16 + lane/4; the lane's 16 B is
+  // covers B rows RA + (wave*4 + j-LA)*16 + lane/4; the lane's 16 B is
   // logical chunk (lane & 3) ^ f(row) of that row's 64-byte K slice.
   const uint16_t* src[L];
 #pragma unroll
@@ -393,7 +393,7 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
   }
   auto copy_one = [&](int t, int stage, int j) {
     const bool isa = j < LA;
-    const int row0 = isa ? (wave * LA + j) * 16 : 256 + (wave * 4 + j - LA) * 16;
+    const int row0 = isa ? (wave * LA + j) * 16 : RA + (wave * 4 + j - LA) * 16;
     dl_copy16(src[j] + t * BK, lds + stage * STAGE + row0 * BK);
   };
 
@@ -420,46 +420,90 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
   const int fhalf = lane >> 5;
   const int nk = c.K / BK;
 
-  bf16x8 fr[2][NQ];
-  auto read_frag = [&](int stage, int s, int buf, int q) {
+  // Fragments: A single-buffered (afr[fm] is refilled with the next step's
+  // fragment as soon as the 4 MFMAs of row fm have been issued), B double
+  // buffered by step parity.  The compiler's own lgkmcnt waits order each
+  // read before its first use.
+  bf16x8 afr[FM];
+  bf16x8 bfr[2][FN];
+  auto read_a = [&](int stage, int s, int fm) {
     const int ch = ((2 * s + fhalf) ^ fsw) * 8;
-    const int row = q < FM ? (wm * FM + q) * 32 + frow : 256 + brow[q - FM] + frow;
-    fr[buf][q] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + ch);
+    const int row = (wm * FM + fm) * 32 + frow;
+    afr[fm] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + ch);
   };
-  auto mfma4 = [&](int buf, int g) {  // MFMAs 4g .. 4g+3 of one step
+  auto read_b = [&](int stage, int s, int buf, int fn) {
+    const int ch = ((2 * s + fhalf) ^ fsw) * 8;
+    const int row = RA + brow[fn] + frow;
+    bfr[buf][fn] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + ch);
+  };
+  auto mfma_row = [&](int buf, int fm) {  // the 4 MFMAs of fragment row fm
 #pragma unroll
-    for (int m = 4 * g; m < 4 * g + 4; m++) {
-      const int fm = m / FN, fn = m % FN;
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][FM + fn], fr[buf][fm],
-                                                            acc[fm][fn], 0, 0, 0);
-    }
+    for (int fn = 0; fn < FN; fn++)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][fn], afr[fm], acc[fm][fn],
+                                                            0, 0, 0);
   };
-  // The copies of a K tile go out in two halves, spread one or two per
-  // group of 4 MFMAs: copies [0, H) of tile t+5 in step 1 of tile t
-  // (right after the barrier frees tile t's stage) and copies [H, L) in
-  // step 0 of tile t+1.  A steady trickle keeps the memory pipeline from
-  // backing up into the MFMA issue.
+  // The copies of a K tile go out in two halves, spread over the MFMA rows:
+  // copies [0, H) of tile t+NS in step 1 of tile t (right after the barrier
+  // frees tile t's stage) and copies [H, L) in step 0 of tile t+1.  A steady
+  // trickle keeps the memory pipeline from backing up into the MFMA issue.
   constexpr int H = (L + 1) / 2;
-  constexpr int CPG = (H + GPS - 1) / GPS;  // copies per group
+  constexpr int CP0 = (L - H + FM - 1) / FM;             // copies per row, step 0
+  constexpr int CP1 = FM > 1 ? (H + FM - 2) / (FM - 1) : H;  // per row after the barrier
 
-  // step 0 of the tile in `stage`: read its step-1 fragments while
-  // multiplying; optionally issue the second half of tile ct's copies
+  // step 0 of the tile in `stage`: multiply, reading the tile's step-1
+  // fragments behind the MFMAs; optionally issue the second half of tile
+  // ct's copies into stage cst
   auto step0 = [&](int stage, bool copy, int ct, int cst) {
 #pragma unroll
-    for (int g = 0; g < GPS; g++) {
+    for (int fm = 0; fm < FM; fm++) {
+      mfma_row(0, fm);
       if (copy)
 #pragma unroll
-        for (int j = H + g * CPG; j < H + (g + 1) * CPG && j < L; j++) copy_one(ct, cst, j);
+        for (int j = H + fm * CP0; j < H + (fm + 1) * CP0 && j < L; j++) copy_one(ct, cst, j);
+      read_a(stage, 1, fm);
 #pragma unroll
-      for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(stage, 1, 1, q);
-      mfma4(0, g);
+      for (int fn = 0; fn < FN; fn++)
+        if (fn % FM == fm) read_b(stage, 1, 1, fn);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  };
+  // step 1: row 0 multiplies before the barrier (this wave's reads of the
+  // tile have then had a full row of MFMAs to land); after it, rows 1.. issue
+  // the first half of tile ct's copies into the freed stage and read tile
+  // t+1's step-0 fragments from stage nst
+  auto step1 = [&](bool more, bool copy, int ct, int cst, int nst, auto wait_fn) {
+    mfma_row(1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      wait_fn();                            // this wave's copies of tile t+1 ...
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // ... and reads of tile t (lgkmcnt(0))
+      __builtin_amdgcn_s_barrier();         // ... and everyone's; tile t fully read
+    }
+#pragma unroll
+    for (int fm = 1; fm <= FM; fm++) {
+      if (fm < FM) mfma_row(1, fm);
+      if (copy)
+#pragma unroll
+        for (int j = (fm - 1) * CP1; j < fm * CP1 && j < H; j++)
+          if (FM > 1 || fm == 1) copy_one(ct, cst, j);
+      if (more) {
+        if (fm == 1) read_a(nst, 0, 0);
+        if (fm < FM) read_a(nst, 0, fm);
+        if (FM == 1 && fm == 1) {
+#pragma unroll
+          for (int fn = 0; fn < FN; fn++) read_b(nst, 0, 0, fn);
+        } else if (fm < FM) {
+#pragma unroll
+          for (int fn = 0; fn < FN; fn++)
+            if (fn % (FM > 1 ? FM - 1 : 1) == fm - 1) read_b(nst, 0, 0, fn);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // prologue: tiles 0..3 and the first half of tile 4 in flight (one tile
-  // per stage), tile 0 published, its step-0 fragments in registers
+  // prologue: tiles 0 .. NS-2 and the first half of tile NS-1 in flight (one
+  // tile per stage), tile 0 published, its step-0 fragments in registers
   const int pro = nk < NS - 1 ? nk : NS - 1;
   for (int t = 0; t < pro; t++)
 #pragma unroll
@@ -467,34 +511,24 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
   if (nk >= NS) {
 #pragma unroll
     for (int j = 0; j < H; j++) copy_one(NS - 1, NS - 1, j);
-    wait_vmcnt<3 * L + H>();
+    wait_vmcnt<(NS - 2) * L + H>();
   } else {
     wait_vmcnt_tiles<L>(nk - 1);
   }
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int q = 0; q < NQ; q++) read_frag(0, 0, 0, q);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  for (int fm = 0; fm < FM; fm++) read_a(0, 0, fm);
+#pragma unroll
+  for (int fn = 0; fn < FN; fn++) read_b(0, 0, 0, fn);
 
   int st = 0;  // stage of tile t
   int t = 0;
-  // steady state: tiles t+4 and t+5 exist
+  // steady state: tiles t+NS-1 and t+NS exist
   for (; t + NS < nk; t++) {
     const int st1 = st == NS - 1 ? 0 : st + 1;
-    const int stp = st == 0 ? NS - 1 : st - 1;  // stage of tile t-1 = tile t+4
+    const int stp = st == 0 ? NS - 1 : st - 1;  // stage of tile t-1 = tile t+NS-1
     step0(st, true, t + NS - 1, stp);
-    wait_vmcnt<(NS - 2) * L>();    // this wave's copies of tile t+1 ...
-    __builtin_amdgcn_s_barrier();  // ... and everyone's; tile t fully read
-#pragma unroll
-    for (int g = 0; g < GPS; g++) {
-#pragma unroll
-      for (int j = g * CPG; j < (g + 1) * CPG && j < H; j++) copy_one(t + NS, st, j);
-#pragma unroll
-      for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(st1, 0, 0, q);
-      mfma4(1, g);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    step1(true, true, t + NS, st, st1, [] { wait_vmcnt<(NS - 2) * L>(); });
     st = st1;
   }
   // drain: at most the second half of the last tile is left to issue
@@ -502,20 +536,8 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
     const int st1 = st == NS - 1 ? 0 : st + 1;
     const int stp = st == 0 ? NS - 1 : st - 1;
     step0(st, t + NS - 1 < nk, t + NS - 1, stp);
-    const bool more = t + 1 < nk;
-    if (more) {
-      wait_vmcnt_tiles<L>(nk - 2 - t);
-      __builtin_amdgcn_s_barrier();
-    }
-#pragma unroll
-    for (int g = 0; g < GPS; g++) {
-      if (more)
-#pragma unroll
-        for (int q = g * RPG; q < (g + 1) * RPG && q < NQ; q++) read_frag(st1, 0, 0, q);
-      mfma4(1, g);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    const int left = nk - 2 - t;  // tiles after t+1, all issued
+    step1(t + 1 < nk, false, 0, 0, st1, [&] { wait_vmcnt_tiles<L>(left); });
     st = st1;
   }
 
@@ -527,9 +549,9 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
 // of expert loads) wastes at most 63 rows of MFMA work.
 template <bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kGemmStages * kGemmStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kGemmLdsElems];
   int tile_id, n_tile;
-  if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
+  if (!work_item(args, tile_id, n_tile)) return;
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
   const int n0 = n_tile * (SWIGLU ? 128 : 256);
   if (n0 >= c.N) return;
@@ -555,7 +577,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
   __shared__ float sa[32][KC + 1];
   __shared__ float sb[NB][KC + 1];
   int tile_id, n_tile;
-  if (!work_item(*args.ntiles, args.n_ntiles, tile_id, n_tile)) return;
+  if (!work_item(args, tile_id, n_tile)) return;
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
   const int n0 = n_tile * 64;
   if (n0 >= c.N) return;
@@ -612,25 +634,74 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
 // ------------------------------------------------------------------------
 // Tile list: routed experts e < E_ffn get ceil(count_e / BM) tiles of
 // sorted positions; shared expert s gets ceil(T / BM) tiles of tokens.
+//
+// Then the XCD schedule of both GEMMs.  The expert GEMMs are bound by the
+// rate at which a CU pulls operand bytes from L2, and a 256-row-path item
+// reads its 256 weight rows whatever its height: timed per block, an item
+// costs about a fixed 3 plus 1 per 64 rows of its variant (4 for 64 rows,
+// 7 for 256).  Tiles of the other paths have one size and cost 1.  XCD x
+// starts at the first item whose cost prefix reaches x/8 of the total.
 // Single block; E_ffn <= 1024.
+__device__ __forceinline__ int tile_cost(int BM, int rows) {
+  return BM == 256 ? (rows + 63) / 64 + 3 : 1;
+}
+
+// Tiles [first, first + n) of one group, all of `full` rows but the last of
+// `last` rows, starting at cost prefix P: writes every XCD boundary that
+// falls in them.  A target t lands in tile i (prefix Pi, cost c) when
+// Pi*nn < t <= (Pi+c)*nn, at item i*nn + ceil((t - Pi*nn) / c).
+__device__ __forceinline__ void place_targets(int first, int n, int full, int last, int BM,
+                                              int64_t P, int64_t total, int nn1, int nn2,
+                                              int32_t* sched) {
+  const uint32_t cf = tile_cost(BM, full), cl = tile_cost(BM, last);
+  // rolled loops: the kernel runs once per layer call on a cold instruction
+  // cache, so its code must stay small; offsets inside one group fit in 32
+  // bits, so the divisions are 32-bit
+#pragma unroll 1
+  for (int g = 0; g < 2; g++) {
+    const uint32_t nn = g == 0 ? nn1 : nn2;
+    const int64_t lo = P * nn, hi = (P + (int64_t)(n - 1) * cf + cl) * nn;
+#pragma unroll 1
+    for (int x = 1; x < kXcds; x++) {
+      const int64_t tgt = (x * total * nn + kXcds - 1) / kXcds;
+      if (tgt <= lo || tgt > hi) continue;
+      // full tiles first, then the last one
+      const uint32_t d = (uint32_t)(tgt - lo);  // in [1, hi - lo]
+      uint32_t i = (d - 1) / (cf * nn);
+      if (i > (uint32_t)(n - 1)) i = n - 1;
+      const uint32_t c = i == (uint32_t)(n - 1) ? cl : cf;
+      const uint32_t r = d - i * cf * nn;       // target minus the tile's prefix, >= 1
+      sched[1 + g * (kXcds + 1) + x] = (int32_t)((first + i) * nn + (r + c - 1) / c);
+    }
+  }
+}
+
 __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ offsets,
                                                       int E_ffn, int n_shared, int64_t T, int BM,
+                                                      int nn1, int nn2,
                                                       int4* __restrict__ tiles,
-                                                      int32_t* __restrict__ ntiles) {
+                                                      int32_t* __restrict__ sched) {
   __shared__ int32_t pre[1024];
+  __shared__ int32_t prc[1024];
   const int e = threadIdx.x;
   const int cnt = e < E_ffn ? offsets[e + 1] - offsets[e] : 0;
   const int nt = (cnt + BM - 1) / BM;
+  const int last = cnt - (nt - 1) * BM;
+  const int ce = nt ? (nt - 1) * tile_cost(BM, BM) + tile_cost(BM, last) : 0;
   pre[e] = nt;
+  prc[e] = ce;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
-    int v = e >= o ? pre[e - o] : 0;
+    const int v = e >= o ? pre[e - o] : 0;
+    const int w = e >= o ? prc[e - o] : 0;
     __syncthreads();
     pre[e] += v;
+    prc[e] += w;
     __syncthreads();
   }
   const int start = pre[e] - nt;
   const int routed_total = pre[1023];
+  const int64_t routed_cost = prc[1023];
   if (e < E_ffn) {
     const int base = offsets[e];
     for (int i = 0; i < nt; i++) {
@@ -639,12 +710,31 @@ __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict_
     }
   }
   const int per_shared = (int)((T + BM - 1) / BM);
+  const int shared_last = (int)(T - (int64_t)(per_shared - 1) * BM);
   for (int j = e; j < n_shared * per_shared; j += 1024) {
     const int s = j / per_shared, i = j % per_shared;
     const int r = i * BM;
     tiles[routed_total + j] = make_int4(E_ffn + s, r, (int)(T - r < BM ? T - r : BM), 0);
   }
-  if (e == 0) *ntiles = routed_total + n_shared * per_shared;
+  const int ntot = routed_total + n_shared * per_shared;
+  const int64_t cs = per_shared ? (int64_t)(per_shared - 1) * tile_cost(BM, BM) +
+                                      tile_cost(BM, shared_last) : 0;
+  const int64_t total = routed_cost + n_shared * cs;
+
+  if (e == 0) {
+    sched[0] = ntot;
+    for (int g = 0; g < 2; g++) {
+      const int nn = g == 0 ? nn1 : nn2;
+      for (int x = 0; x < kXcds; x++) sched[1 + g * (kXcds + 1) + x] = 0;  // targets of an empty list
+      sched[1 + g * (kXcds + 1) + kXcds] = ntot * nn;
+    }
+  }
+  __syncthreads();
+  if (e < E_ffn && nt > 0)
+    place_targets(start, nt, BM, last, BM, prc[e] - ce, total, nn1, nn2, sched);
+  if (e < n_shared && per_shared > 0)
+    place_targets(routed_total + e * per_shared, per_shared, BM, shared_last, BM,
+                  routed_cost + e * cs, total, nn1, nn2, sched);
 }
 
 // ------------------------------------------------------------------------
@@ -660,11 +750,17 @@ int64_t gemm_max_tiles(int64_t T, int k, int E_ffn, int n_shared, int BM) {
   return cdiv(T * k, BM) + E_ffn + n_shared * cdiv(T, BM);
 }
 
+int gemm_n_ntiles(int dtype, bool swiglu, int N) {
+  // output columns per tile: fp32 64; bf16 256 B rows = 128 gated / 256 plain
+  const int bno = dtype == MOE_F32 ? 64 : (swiglu ? 128 : 256);
+  return N > 0 ? (int)cdiv(N, bno) : 1;
+}
+
 hipError_t launch_build_tiles(const int32_t* offsets, int E_ffn,
-                              int n_shared, int64_t T, int BM, int4* tiles, int32_t* ntiles,
-                              hipStream_t st) {
+                              int n_shared, int64_t T, int BM, int nn1, int nn2, int4* tiles,
+                              int32_t* sched, hipStream_t st) {
   hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, st, offsets, E_ffn, n_shared,
-                     T, BM, tiles, ntiles);
+                     T, BM, nn1, nn2, tiles, sched);
   return hipGetLastError();
 }
 
@@ -673,12 +769,12 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a
   GemmArgs a = a_in;
   const int Nmax = a.N_routed > a.N_shared ? a.N_routed : a.N_shared;
   if (max_tiles == 0 || Nmax == 0) return hipSuccess;
-  int bno;
-  if (dtype == MOE_F32) bno = 64;
-  else bno = swiglu ? 128 : 256;  // BN = 256 B rows per tile
-  a.n_ntiles = (int)cdiv(Nmax, bno);
-  // one block per work item, padded so every XCD chunk is covered
-  const unsigned grid = (unsigned)(max_tiles * a.n_ntiles + 8);
+  a.n_ntiles = gemm_n_ntiles(dtype, swiglu, Nmax);
+  // enough blocks for the longest XCD range: a range holds about 1/8 of the
+  // cost, and on the 256-row path an item costs 4 to 7 (elsewhere 1)
+  const int64_t W = max_tiles * a.n_ntiles;
+  const int64_t per_xcd = (BM == 256 ? cdiv(7 * W, 4 * kXcds) : cdiv(W, kXcds)) + 2;
+  const unsigned grid = (unsigned)(per_xcd * kXcds);
   if (dtype == MOE_F32) {
     if (swiglu)
       hipLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3(grid), dim3(256), 0, st, a);

@@ -5,9 +5,17 @@
 
 namespace moe {
 
+// Work schedule written by the tile builder, on device: [0] = number of M
+// tiles; [1 + 9 g + x] = first work item of XCD x (x = 0..7) for GEMM g
+// (g = 0: the gated GEMM, 1: the down projection), [1 + 9 g + 8] = number of
+// work items.  A work item is one (M tile, N tile) pair, M-tile major.
+constexpr int kXcds = 8;
+constexpr int kSchedInts = 1 + 2 * (kXcds + 1);
+
 struct GemmArgs {
-  const int4* tiles;       // {group, first row, rows, 0}
-  const int32_t* ntiles;   // device count of valid tiles
+  const int4* tiles;         // {group, first row, rows, 0}
+  const int32_t* ntiles;     // device count of valid tiles (schedule entry 0)
+  const int32_t* xcd_first;  // this GEMM's 9 XCD boundaries in the schedule
   int E_ffn;
   int64_t T;
   // A operand
@@ -66,8 +74,10 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
 // gemm.hip
 int gemm_tile_rows(int dtype, int64_t tasks, int E_ffn);
 int64_t gemm_max_tiles(int64_t T, int k, int E_ffn, int n_shared, int BM);
+int gemm_n_ntiles(int dtype, bool swiglu, int N);
 hipError_t launch_build_tiles(const int32_t* offsets, int E_ffn,
-                              int n_shared, int64_t T, int BM, int4* tiles, int32_t* ntiles,
+                              int n_shared, int64_t T, int BM, int nn1, int nn2, int4* tiles,
+                              int32_t* sched,
                               hipStream_t st);
 hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a,
                                int64_t max_tiles, hipStream_t st);
