@@ -27,15 +27,16 @@ COPY_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def measured_traffic(workload, kernel_sha):
+def measured_traffic(workload, kernel):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if there is none or the kernel source changed since."""
+    summary, or None if there is none or the kernel's source changed since."""
+    from mixture_experts_layer_22_amd import profiling as P
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_sha:
+    if rec.get("kernel") != kernel or rec.get("source_sha256") != P.kernel_source_sha(kernel):
         return None
     return rec.get("bytes")
 
@@ -51,8 +52,12 @@ def algorithmic_work(cfg, counts):
     if cfg.router == 1:
         n = T * cfg.k
         touched = int(np.count_nonzero(counts))
+        es = 2 if cfg.dtype == 1 else 4
+        # k_atomic_h reads each touched expert's in-vector and each token once
+        # and writes one fp32 activation per task
         return {"expert1_flop": 2.0 * d * n, "expert2_flop": 2.0 * d * n,
-                "weight_bytes": touched * 2 * d * 2}
+                "weight_bytes": touched * d * es,
+                "atomic_h_bytes": (touched + T) * d * es + n * 4}
     n_ffn = int(np.sum(counts[:cfg.E_ffn]))
     touched = int(np.count_nonzero(counts[:cfg.E_ffn]))
     es = 2 if cfg.dtype == 1 else 4
@@ -61,6 +66,10 @@ def algorithmic_work(cfg, counts):
         "expert1_flop": 4.0 * d * rows_f,
         "expert2_flop": 2.0 * d * rows_f,
         "weight_bytes": (touched * 3 * d * cfg.f + cfg.n_shared * 3 * d * cfg.f_shared) * es,
+        # the gated GEMM's operands: weights of touched experts, the tokens,
+        # its output H
+        "gemm1_bytes": ((touched * 2 * d * cfg.f + cfg.n_shared * 2 * d * cfg.f_shared) + T * d
+                        + n_ffn * cfg.f + T * cfg.n_shared * cfg.f_shared) * es,
     }
 
 
@@ -108,7 +117,6 @@ def main():
     import torch
     from mixture_experts_layer_22_amd import binding as B
     from mixture_experts_layer_22_amd import inputs as I
-    from mixture_experts_layer_22_amd import profiling as P
 
     if args.calibrate_copy:
         n = COPY_BYTES // 4
@@ -174,22 +182,24 @@ def main():
 
     if cfg.router == 1:
         # atomic layer: the expert stage is bound by HBM
-        ach = work["weight_bytes"] / (phase_us["expert1"] * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": "k_atomic_h", "achieved": ach, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None}
-    elif T * cfg.k / max(cfg.E_ffn, 1) < 64:
-        # decode-sized: weight streaming
-        us = phase_us["expert1"] + phase_us["expert2"]
-        ach = work["weight_bytes"] / (us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": "grouped GEMM1+GEMM2", "achieved": ach,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                "traffic": None}
+        kern = f"k_atomic_h<{'unsigned short' if cfg.dtype == 1 else 'float'}>"
+        ach = work["atomic_h_bytes"] / (phase_us["expert1"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": kern, "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+    elif T * cfg.k / max(cfg.E_ffn, 1) < 64 or cfg.dtype != 1:
+        # decode-sized (and fp32) layers: the gated GEMM streams its weights
+        kern = "k_grouped_gemm_bf16<1, 4, 1, 2, true>" if cfg.dtype == 1 else \
+            "k_grouped_gemm_f32<true>"
+        ach = work["gemm1_bytes"] / (phase_us["expert1"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": kern, "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
     else:
+        kern = "k_gemm_dl<true>"
         ach = work["expert1_flop"] / (phase_us["expert1"] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": "k_grouped_gemm_bf16 (GEMM1 + SiLU gate)",
+        roof = {"bound": "mfma", "kernel": kern + " (gated GEMM + SiLU)",
                 "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
-    roof["traffic"] = measured_traffic(cfg.name, P.kernel_source_sha())
+                "frac": ach / PEAK_BF16_TFLOPS}
+    roof["traffic"] = measured_traffic(cfg.name, kern)
     expert_flop = work["expert1_flop"] + work["expert2_flop"]
     line = {
         "metric": METRIC,

@@ -6,7 +6,7 @@
            [--copy-bytes N] [--out FILE] [--cmd CMD]
 
 `stats` turns a `--kernel-trace --stats` run (CSV output) into a short text
-table.  `traffic` turns two counter runs of a workload (FETCH_SIZE, then
+table (with the bench line's phase times, when the run's log is given).  `traffic` turns two counter runs of a workload (FETCH_SIZE, then
 WRITE_SIZE) into HBM bytes per launch of one kernel, each scaled by what the
 same counter reads for a plain device copy of known size (the copy moves
 copy_bytes in and copy_bytes out), and writes a JSON record that bench.py
@@ -26,8 +26,24 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def kernel_source_sha(path: str = os.path.join(HERE, "csrc", "gemm.hip")) -> str:
-    with open(path, "rb") as f:
+# source file of each kernel whose traffic is recorded
+KERNEL_SOURCES = {
+    "k_gemm_dl": "gemm.hip",
+    "k_grouped_gemm_bf16": "gemm.hip",
+    "k_grouped_gemm_f32": "gemm.hip",
+    "k_atomic_h": "combine.hip",
+}
+
+
+def kernel_source(kernel: str) -> str:
+    for k, f in KERNEL_SOURCES.items():
+        if kernel.startswith(k):
+            return f
+    raise KeyError(kernel)
+
+
+def kernel_source_sha(kernel: str = "k_gemm_dl") -> str:
+    with open(os.path.join(HERE, "csrc", kernel_source(kernel)), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -82,7 +98,8 @@ def traffic_record(kernel, copy_fetch, copy_write, fetch, write, copy_bytes, cop
         "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": copy_bytes,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "dispatches": [nf, nw],
-        "source_sha256": kernel_source_sha(),
+        "source": kernel_source(kernel),
+        "source_sha256": kernel_source_sha(kernel),
     }
 
 
@@ -93,6 +110,7 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--out")
     s.add_argument("--cmd", default="")
+    s.add_argument("--log", help="the profiled bench run's output (for its phase times)")
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
     t.add_argument("--copy-fetch", required=True)
@@ -106,6 +124,13 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd_name == "stats":
         text = stats_table(a.dir)
+        if a.log:
+            for line in open(a.log):
+                if line.startswith("{") and '"phases_us"' in line:
+                    rec = json.loads(line)
+                    ph = ", ".join(f"{k} {v:.1f}" for k, v in rec["phases_us"].items())
+                    text += (f"\n\nbench line of the same run: {rec['ms_per_step'] * 1e3:.1f} us per step; "
+                             f"phases (us, HIP events): {ph}")
         if a.cmd:
             text = f"command: {a.cmd}\n\n{text}\n"
     else:
