@@ -33,13 +33,15 @@ struct TileCtx {
   int N, K;
 };
 
+// Tile descriptors describe the tile's group: {group, first row, rows, first
+// tile}; M tile g of the group covers rows [g*bm, min((g+1)*bm, rows)).
 template <bool SWIGLU>
-__device__ __forceinline__ TileCtx<SWIGLU> tile_ctx(const GemmArgs& a, int4 t) {
+__device__ __forceinline__ TileCtx<SWIGLU> tile_ctx(const GemmArgs& a, int4 t, int g) {
   TileCtx<SWIGLU> c;
   c.shared = t.x >= a.E_ffn;
   c.e = c.shared ? t.x - a.E_ffn : t.x;
-  c.r0 = t.y;
-  c.nr = t.z;
+  c.r0 = (int64_t)t.y + (int64_t)g * a.bm;
+  c.nr = t.z - g * a.bm < a.bm ? t.z - g * a.bm : a.bm;
   c.N = c.shared ? a.N_shared : a.N_routed;
   c.K = c.shared ? a.K_shared : a.K_routed;
   return c;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
   int tile_id, n_tile;
   if (!work_item(args, tile_id, n_tile)) return;
   const int4 tl = args.tiles[tile_id];
-  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl);
+  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl, tile_id - tl.w);
   const int n0 = n_tile * BNO;
   if (n0 >= c.N) return;
 
@@ -243,18 +245,22 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
 // lane i of a wave lands 16 bytes at LDS base + 16 i.  K advances in 32-wide
 // tiles held in a ring of five LDS stages of 32 KB (A rows [0, 256), B rows
 // [256, 512), 64 B per row), i.e. all 160 KB of the CU's LDS.  A K tile is
-// two 16-wide MFMA steps; the fragments of the next step are read while the
-// current one multiplies (double buffered in registers).
+// one v_mfma_f32_16x16x32_bf16 step.
 //
-// One barrier per K tile, between its two steps: it publishes tile t+1 (each
-// wave first waits for its own copies) and certifies that every wave holds
-// tile t's last fragments, so tile t's stage can take tile t+5.  A copy is
-// issued three to four K tiles (six to eight steps) before it is needed.
+// Eight waves, two per SIMD, each owning BMT/2 rows x 64 B rows (128
+// accumulator registers).  On CDNA4 the 32x32x16 MFMA shape stalls the
+// vector-memory path that feeds LDS while it runs, and one wave per SIMD
+// cannot issue MFMAs while its own copy instructions wait to issue; the
+// 16x16x32 shape with two waves per SIMD keeps the copies and the MFMAs
+// overlapped (measured: the same copy + MFMA mix runs in 0.7x the time).
+//
+// One barrier per K tile: it publishes tile t+1 (each wave first waits for
+// its own copies) and certifies that every wave holds tile t's fragments, so
+// tile t's stage takes tile t+5 right away: copies run four K tiles ahead.
 //
 // LDS rows are 4 chunks of 16 B; chunk c of row r sits at c ^ f(r),
-// f(r) = ((r >> 1) & 3) ^ ((r >> 2) & 3).  An MFMA fragment read (32
-// consecutive rows, one chunk) then touches distinct banks within every 8
-// lanes (32 x 4-byte banks) and within every 16 lanes (64 banks).
+// f(r) = ((r >> 1) & 3) ^ ((r >> 2) & 3).  A fragment read (16 consecutive
+// rows x 4 chunks, 1 KB) touches distinct banks within every 16 lanes.
 //
 // Rows past the group's end (A) or past N (B) are pointed at a valid row:
 // their products only reach output rows / columns that are not stored.
@@ -288,53 +294,53 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int n) {
 
 constexpr int kGemmLdsElems = 81920;  // 160 KB: all of the CU's LDS
 
-// Epilogue.  acc[fm][fn][e] = C[row = (wm*FM + fm)*32 + lane%32]
-//                               [col = fn*32 + 8(e/4) + 4(lane/32) + e%4]
-// (col relative to the wave's first column).  The bf16 tile (BMT x BNO, at
-// most 128 KB) is staged in the idle K stages, then written out as whole
+constexpr int kGemmThreads = 512;
+constexpr int kGroupWindow = 32;  // blocks an XCD runs at once (one per CU)
+
+// Epilogue.  With the weight fragment as the MFMA's first operand, lane l of
+// acc[fm][fn] holds output row wm*BMT/2 + fm*16 + l%16 and the 4 output
+// columns brow(fn) + 4(l/16) .. +3 (for the gated GEMM, the gate block fn
+// and the up block fn+2 cover the same columns).  The bf16 tile (BMT x BNO,
+// at most 128 KB) is staged in the idle K stages, then written out as whole
 // rows with 16-byte stores.  In LDS a row is BNO/4 slots of 8 bytes (4
-// columns); slot s of row r sits at s ^ (r & 31), so the 32 rows of a
-// fragment land in distinct banks.
+// columns); slot s of row r sits at s ^ (r & 31).
 template <int BMT, bool SWIGLU, int FM, int FN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const TileCtx<SWIGLU>& c,
-                                              int n0, uint16_t* lds, const f32x16 (&acc)[FM][FN],
+                                              int n0, uint16_t* lds, const f32x4 (&acc)[FM][FN],
                                               int wm, int wn) {
   constexpr int BNO = SWIGLU ? 128 : 256;
   constexpr int SLOTS = BNO / 4;
   constexpr int CPR = BNO / 8;
   static_assert(BMT * BNO <= kGemmLdsElems, "epilogue staging");
   const int tid = threadIdx.x, lane = tid & 63;
-  const int frow = lane & 31, fhalf = lane >> 5;
+  const int frow = lane & 15, fq = lane >> 4;
   uint2* s8 = reinterpret_cast<uint2*>(lds);
   __syncthreads();  // every wave is past its last fragment read
 #pragma unroll
   for (int fm = 0; fm < FM; fm++) {
-    const int row = (wm * FM + fm) * 32 + frow;
+    const int row = wm * (BMT / 2) + fm * 16 + frow;
     uint2* srow = s8 + row * SLOTS;
     if (SWIGLU) {
 #pragma unroll
-      for (int fn = 0; fn < 2; fn++)
+      for (int fn = 0; fn < 2; fn++) {
+        const int slot = (wn * 32 + fn * 16) / 4 + fq;
+        float h[4];
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const int slot = ((wn * 2 + fn) * 32 + 8 * g + 4 * fhalf) / 4;
-          float h[4];
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const float gt = acc[fm][fn][4 * g + e], up = acc[fm][fn + 2][4 * g + e];
-            h[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
-          }
-          srow[slot ^ frow] = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+        for (int e = 0; e < 4; e++) {
+          const float gt = acc[fm][fn][e], up = acc[fm][fn + 2][e];
+          h[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
         }
+        srow[slot ^ (row & 31)] = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+      }
     } else {
 #pragma unroll
-      for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const int slot = ((wn * FN + fn) * 32 + 8 * g + 4 * fhalf) / 4;
-          srow[slot ^ frow] = make_uint2(pack_bf16x2(acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1]),
-                                         pack_bf16x2(acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]));
-        }
+      for (int fn = 0; fn < FN; fn++) {
+        const int slot = (wn * 64 + fn * 16) / 4 + fq;
+        srow[slot ^ (row & 31)] = make_uint2(pack_bf16x2(acc[fm][fn][0], acc[fm][fn][1]),
+                                             pack_bf16x2(acc[fm][fn][2], acc[fm][fn][3]));
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);  // one fragment row at a time
   }
   __syncthreads();
   // 16-byte chunk j of row r is slots 2j, 2j+1: one aligned 16-byte read at
@@ -342,7 +348,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const TileCt
   const int nrows = c.nr < BMT ? c.nr : BMT;
   const bool full_cols = n0 + BNO <= c.N;
 #pragma unroll 4
-  for (int i = tid; i < nrows * CPR; i += 256) {
+  for (int i = tid; i < nrows * CPR; i += kGemmThreads) {
     const int r = i / CPR, j = i - (i / CPR) * CPR;
     const int col = n0 + 8 * j;
     if (!full_cols && col >= c.N) continue;
@@ -353,8 +359,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const TileCt
 }
 
 // One tile of BMT (64, 128, 192 or 256) rows x 256 B rows.  Waves form a
-// 2 x 2 grid; a wave owns BMT/2 rows and 128 B rows (FM x 4 fragments of
-// 32x32, i.e. up to all 256 AGPRs of accumulators).
+// 2 (rows) x 4 (B rows) grid; a wave owns BMT/2 rows in FM = BMT/32 blocks
+// of 16 and 64 B rows in 4 blocks of 16 (for the gated GEMM: 32 gate rows
+// and the same 32 columns' up rows).
 template <int BMT, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx<SWIGLU>& c,
                                              int n0, uint16_t* lds) {
@@ -362,24 +369,31 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
   constexpr int RA = 256;                    // LDS rows of A; B rows follow
   constexpr int NS = 5;                      // stages in the ring
   constexpr int STAGE = (RA + BN) * BK;
+  constexpr int NW = kGemmThreads / 64;
+  constexpr int FM = BMT / 32, FN = 4;
+  constexpr int CA = BMT / 16;               // A copies (16 rows x 64 B) per K tile
+  constexpr int CT = CA + BN / 16;           // all copies of a K tile
+  constexpr int LMAX = (CT + NW - 1) / NW;   // copies per wave per K tile: LMIN or LMAX
+  constexpr int LMIN = CT / NW;
   static_assert(NS * STAGE <= kGemmLdsElems && BMT % 64 == 0 && BMT <= RA, "LDS ring");
-  constexpr int FM = BMT / 64, FN = 4;
-  constexpr int LA = BMT / 64;               // A copies (16 rows x 64 B) per wave per K tile
-  constexpr int L = LA + 4;                  // + 4 B copies
-  static_assert(4 * L < 64, "vmcnt range");
+  static_assert(4 * LMAX < 64, "vmcnt range");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // loader: copy j < LA covers A rows (wave*LA + j)*16 + lane/4, copy j >= LA
-  // covers B rows RA + (wave*4 + j-LA)*16 + lane/4; the lane's 16 B is
-  // logical chunk (lane & 3) ^ f(row) of that row's 64-byte K slice.
-  const uint16_t* src[L];
+  // loader: this wave's copy i is block copy j = wave + NW*i (if j < CT);
+  // j < CA covers A rows j*16 + lane/4, the rest B rows (j-CA)*16 + lane/4;
+  // the lane's 16 B is logical chunk (lane & 3) ^ f(row) of the row's 64-byte
+  // K slice.  Waves with fewer copies wait with the smaller count (a wait
+  // for more of their own copies than needed, never fewer).
+  const uint16_t* src[LMAX];
 #pragma unroll
-  for (int j = 0; j < L; j++) {
-    const bool isa = j < LA;
-    const int r = (isa ? (wave * LA + j) : (wave * 4 + j - LA)) * 16 + (lane >> 2);
+  for (int i = 0; i < LMAX; i++) {
+    int j = wave + NW * i;
+    if (j >= CT) j = CT - 1;  // unused
+    const bool isa = j < CA;
+    const int r = (isa ? j : j - CA) * 16 + (lane >> 2);
     const int chunk = (lane & 3) ^ lds_swz(r);
     const uint16_t* p;
     if (isa) {
@@ -389,90 +403,58 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
       p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, r);
       if (!p) p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, SWIGLU && r >= BN / 2 ? BN / 2 : 0);
     }
-    src[j] = p + chunk * 8;
+    src[i] = p + chunk * 8;
   }
-  auto copy_one = [&](int t, int stage, int j) {
-    const bool isa = j < LA;
-    const int row0 = isa ? (wave * LA + j) * 16 : RA + (wave * 4 + j - LA) * 16;
-    dl_copy16(src[j] + t * BK, lds + stage * STAGE + row0 * BK);
+  auto copy_one = [&](int t, int stage, int i) {
+    const int j = wave + NW * i;
+    if (j < CT) {
+      const int row0 = j < CA ? j * 16 : RA + (j - CA) * 16;
+      dl_copy16(src[i] + t * BK, lds + stage * STAGE + row0 * BK);
+    }
   };
 
-  // Accumulators hold C^T fragments: the weight fragment is the MFMA's first
-  // operand, so lane l ends up with 4 consecutive output columns of one
-  // output row per 4-element group.
-  f32x16 acc[FM][FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; i++)
 #pragma unroll
-    for (int j = 0; j < FN; j++) acc[i][j] = f32x16{};
+    for (int j = 0; j < FN; j++) acc[i][j] = f32x4{};
 
   int brow[FN];
 #pragma unroll
-  for (int fn = 0; fn < FN; fn++) {
-    if (SWIGLU) {
-      brow[fn] = (fn < 2) ? (wn * 2 + fn) * 32 : BN / 2 + (wn * 2 + fn - 2) * 32;
-    } else {
-      brow[fn] = (wn * FN + fn) * 32;
-    }
-  }
-  const int frow = lane & 31;
-  const int fsw = lds_swz(frow);
-  const int fhalf = lane >> 5;
+  for (int fn = 0; fn < FN; fn++)
+    brow[fn] = SWIGLU ? (fn < 2 ? wn * 32 + fn * 16 : BN / 2 + wn * 32 + (fn - 2) * 16)
+                      : wn * 64 + fn * 16;
+  const int frow = lane & 15;
+  const int fch = ((lane >> 4) ^ lds_swz(frow)) * 8;
   const int nk = c.K / BK;
 
-  // Fragments: A single-buffered (afr[fm] is refilled with the next step's
-  // fragment as soon as the 4 MFMAs of row fm have been issued), B double
-  // buffered by step parity.  The compiler's own lgkmcnt waits order each
-  // read before its first use.
+  // Fragments, single-buffered: afr[fm] is refilled with the next tile's
+  // fragment once the 4 MFMAs of row fm are issued, the B fragments after
+  // the last row (the other wave on the SIMD covers the wait for them).  The
+  // compiler's own lgkmcnt waits order each read before its first use.
   bf16x8 afr[FM];
-  bf16x8 bfr[2][FN];
-  auto read_a = [&](int stage, int s, int fm) {
-    const int ch = ((2 * s + fhalf) ^ fsw) * 8;
-    const int row = (wm * FM + fm) * 32 + frow;
-    afr[fm] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + ch);
+  bf16x8 bfr[FN];
+  auto read_a = [&](int stage, int fm) {
+    const int row = wm * (BMT / 2) + fm * 16 + frow;
+    afr[fm] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + fch);
   };
-  auto read_b = [&](int stage, int s, int buf, int fn) {
-    const int ch = ((2 * s + fhalf) ^ fsw) * 8;
+  auto read_b = [&](int stage, int fn) {
     const int row = RA + brow[fn] + frow;
-    bfr[buf][fn] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + ch);
+    bfr[fn] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + fch);
   };
-  auto mfma_row = [&](int buf, int fm) {  // the 4 MFMAs of fragment row fm
+  auto mfma_row = [&](int fm) {  // the 4 MFMAs of fragment row fm
 #pragma unroll
     for (int fn = 0; fn < FN; fn++)
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][fn], afr[fm], acc[fm][fn],
-                                                            0, 0, 0);
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], afr[fm], acc[fm][fn], 0, 0, 0);
   };
-  // The copies of a K tile go out in two halves, spread over the MFMA rows:
-  // copies [0, H) of tile t+NS in step 1 of tile t (right after the barrier
-  // frees tile t's stage) and copies [H, L) in step 0 of tile t+1.  A steady
-  // trickle keeps the memory pipeline from backing up into the MFMA issue.
-  constexpr int H = (L + 1) / 2;
-  constexpr int CP0 = (L - H + FM - 1) / FM;             // copies per row, step 0
-  constexpr int CP1 = FM > 1 ? (H + FM - 2) / (FM - 1) : H;  // per row after the barrier
+  constexpr int CPR = (LMAX + FM - 2) / (FM > 1 ? FM - 1 : 1);  // copies per row after the barrier
 
-  // step 0 of the tile in `stage`: multiply, reading the tile's step-1
-  // fragments behind the MFMAs; optionally issue the second half of tile
-  // ct's copies into stage cst
-  auto step0 = [&](int stage, bool copy, int ct, int cst) {
-#pragma unroll
-    for (int fm = 0; fm < FM; fm++) {
-      mfma_row(0, fm);
-      if (copy)
-#pragma unroll
-        for (int j = H + fm * CP0; j < H + (fm + 1) * CP0 && j < L; j++) copy_one(ct, cst, j);
-      read_a(stage, 1, fm);
-#pragma unroll
-      for (int fn = 0; fn < FN; fn++)
-        if (fn % FM == fm) read_b(stage, 1, 1, fn);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // step 1: row 0 multiplies before the barrier (this wave's reads of the
-  // tile have then had a full row of MFMAs to land); after it, rows 1.. issue
-  // the first half of tile ct's copies into the freed stage and read tile
-  // t+1's step-0 fragments from stage nst
-  auto step1 = [&](bool more, bool copy, int ct, int cst, int nst, auto wait_fn) {
-    mfma_row(1, 0);
+  // One K tile (in `stage`).  Row 0 multiplies before the barrier (this
+  // wave's reads of the tile have then had a row of MFMAs to land); after
+  // it, rows 1.. issue tile ct's copies into the freed stage and read tile
+  // t+1's A fragments from stage nst, its B fragments after the last row.
+  auto tile = [&](bool more, bool copy, int ct, int cst, int nst, auto wait_fn) {
+    mfma_row(0);
     __builtin_amdgcn_sched_barrier(0);
     if (more) {
       wait_fn();                            // this wave's copies of tile t+1 ...
@@ -481,64 +463,49 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
     }
 #pragma unroll
     for (int fm = 1; fm <= FM; fm++) {
-      if (fm < FM) mfma_row(1, fm);
+      if (fm < FM) mfma_row(fm);
       if (copy)
 #pragma unroll
-        for (int j = (fm - 1) * CP1; j < fm * CP1 && j < H; j++)
-          if (FM > 1 || fm == 1) copy_one(ct, cst, j);
+        for (int i = (fm - 1) * CPR; i < fm * CPR && i < LMAX; i++)
+          if (FM > 1 || fm == 1) copy_one(ct, cst, i);
       if (more) {
-        if (fm == 1) read_a(nst, 0, 0);
-        if (fm < FM) read_a(nst, 0, fm);
-        if (FM == 1 && fm == 1) {
+        if (fm == 1) read_a(nst, 0);
+        if (fm < FM) read_a(nst, fm);
+        if (fm == FM)
 #pragma unroll
-          for (int fn = 0; fn < FN; fn++) read_b(nst, 0, 0, fn);
-        } else if (fm < FM) {
-#pragma unroll
-          for (int fn = 0; fn < FN; fn++)
-            if (fn % (FM > 1 ? FM - 1 : 1) == fm - 1) read_b(nst, 0, 0, fn);
-        }
+          for (int fn = 0; fn < FN; fn++) read_b(nst, fn);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // prologue: tiles 0 .. NS-2 and the first half of tile NS-1 in flight (one
-  // tile per stage), tile 0 published, its step-0 fragments in registers
-  const int pro = nk < NS - 1 ? nk : NS - 1;
+  // prologue: tiles 0 .. NS-1 in flight (tile t in stage t), tile 0
+  // published, its fragments in registers
+  const int pro = nk < NS ? nk : NS;
+#pragma unroll 1
   for (int t = 0; t < pro; t++)
 #pragma unroll
-    for (int j = 0; j < L; j++) copy_one(t, t, j);
-  if (nk >= NS) {
-#pragma unroll
-    for (int j = 0; j < H; j++) copy_one(NS - 1, NS - 1, j);
-    wait_vmcnt<(NS - 2) * L + H>();
-  } else {
-    wait_vmcnt_tiles<L>(nk - 1);
-  }
+    for (int i = 0; i < LMAX; i++) copy_one(t, t, i);
+  wait_vmcnt_tiles<LMIN>(pro - 1);
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int fm = 0; fm < FM; fm++) read_a(0, 0, fm);
+  for (int fm = 0; fm < FM; fm++) read_a(0, fm);
 #pragma unroll
-  for (int fn = 0; fn < FN; fn++) read_b(0, 0, 0, fn);
+  for (int fn = 0; fn < FN; fn++) read_b(0, fn);
 
   int st = 0;  // stage of tile t
   int t = 0;
-  // steady state: tiles t+NS-1 and t+NS exist
+  auto next = [](int x) { return x == NS - 1 ? 0 : x + 1; };
+  // steady state: tile t+NS exists
   for (; t + NS < nk; t++) {
-    const int st1 = st == NS - 1 ? 0 : st + 1;
-    const int stp = st == 0 ? NS - 1 : st - 1;  // stage of tile t-1 = tile t+NS-1
-    step0(st, true, t + NS - 1, stp);
-    step1(true, true, t + NS, st, st1, [] { wait_vmcnt<(NS - 2) * L>(); });
-    st = st1;
+    tile(true, true, t + NS, st, next(st), [] { wait_vmcnt<(NS - 2) * LMIN>(); });
+    st = next(st);
   }
-  // drain: at most the second half of the last tile is left to issue
+  // drain: every copy is issued; tiles after t+1 left in flight: nk-2-t
   for (; t < nk; t++) {
-    const int st1 = st == NS - 1 ? 0 : st + 1;
-    const int stp = st == 0 ? NS - 1 : st - 1;
-    step0(st, t + NS - 1 < nk, t + NS - 1, stp);
-    const int left = nk - 2 - t;  // tiles after t+1, all issued
-    step1(t + 1 < nk, false, 0, 0, st1, [&] { wait_vmcnt_tiles<L>(left); });
-    st = st1;
+    const int left = nk - 2 - t;
+    tile(t + 1 < nk, false, 0, 0, next(st), [&] { wait_vmcnt_tiles<LMIN>(left); });
+    st = next(st);
   }
 
   gemm_epilogue<BMT, SWIGLU, FM, FN>(args, c, n0, lds, acc, wm, wn);
@@ -548,11 +515,27 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
 // rows, so the last tile of a group (and the small groups of the long tail
 // of expert loads) wastes at most 63 rows of MFMA work.
 template <bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void k_gemm_dl(GemmArgs args) {
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dl(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kGemmLdsElems];
   int tile_id, n_tile;
   if (!work_item(args, tile_id, n_tile)) return;
-  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
+  // Inside its group the item list is walked N chunk by N chunk: a chunk
+  // holds all G M tiles of the group times about 32/G N tiles, so the ~32
+  // blocks an XCD runs at once share both their gathered rows and their
+  // weight tiles in L2 (a group with many N tiles walked M-tile major
+  // would have them all read different weights).
+  const int4 tl = args.tiles[tile_id];
+  const int nn = args.n_ntiles;
+  const int G = (tl.z + args.bm - 1) / args.bm;
+  const int u = (tile_id - tl.w) * nn + n_tile;  // M-major index inside the group
+  int gw = (kGroupWindow + G - 1) / G;
+  gw = gw < 1 ? 1 : (gw > nn ? nn : gw);
+  const int chunk = u / (G * gw);
+  const int cw = nn - chunk * gw < gw ? nn - chunk * gw : gw;  // the last chunk may be narrower
+  const int v = u - chunk * G * gw;
+  const int g = v / cw;
+  n_tile = chunk * gw + (v - g * cw);
+  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl, g);
   const int n0 = n_tile * (SWIGLU ? 128 : 256);
   if (n0 >= c.N) return;
   if (c.nr > 192)
@@ -578,7 +561,8 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
   __shared__ float sb[NB][KC + 1];
   int tile_id, n_tile;
   if (!work_item(args, tile_id, n_tile)) return;
-  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, args.tiles[tile_id]);
+  const int4 tl = args.tiles[tile_id];
+  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl, tile_id - tl.w);
   const int n0 = n_tile * 64;
   if (n0 >= c.N) return;
   const int tid = threadIdx.x;
@@ -633,7 +617,8 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
 
 // ------------------------------------------------------------------------
 // Tile list: routed experts e < E_ffn get ceil(count_e / BM) tiles of
-// sorted positions; shared expert s gets ceil(T / BM) tiles of tokens.
+// sorted positions; shared expert s gets ceil(T / BM) tiles of tokens.  Each
+// tile's descriptor names its whole group (see tile_ctx).
 //
 // Then the XCD schedule of both GEMMs.  The expert GEMMs are bound by the
 // rate at which a CU pulls operand bytes from L2, and a 256-row-path item
@@ -704,17 +689,13 @@ __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict_
   const int64_t routed_cost = prc[1023];
   if (e < E_ffn) {
     const int base = offsets[e];
-    for (int i = 0; i < nt; i++) {
-      const int r = i * BM;
-      tiles[start + i] = make_int4(e, base + r, cnt - r < BM ? cnt - r : BM, 0);
-    }
+    for (int i = 0; i < nt; i++) tiles[start + i] = make_int4(e, base, cnt, start);
   }
   const int per_shared = (int)((T + BM - 1) / BM);
   const int shared_last = (int)(T - (int64_t)(per_shared - 1) * BM);
   for (int j = e; j < n_shared * per_shared; j += 1024) {
-    const int s = j / per_shared, i = j % per_shared;
-    const int r = i * BM;
-    tiles[routed_total + j] = make_int4(E_ffn + s, r, (int)(T - r < BM ? T - r : BM), 0);
+    const int s = j / per_shared;
+    tiles[routed_total + j] = make_int4(E_ffn + s, 0, (int)T, routed_total + s * per_shared);
   }
   const int ntot = routed_total + n_shared * per_shared;
   const int64_t cs = per_shared ? (int64_t)(per_shared - 1) * tile_cost(BM, BM) +
@@ -770,6 +751,7 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a
   const int Nmax = a.N_routed > a.N_shared ? a.N_routed : a.N_shared;
   if (max_tiles == 0 || Nmax == 0) return hipSuccess;
   a.n_ntiles = gemm_n_ntiles(dtype, swiglu, Nmax);
+  a.bm = BM;
   // enough blocks for the longest XCD range: a range holds about 1/8 of the
   // cost, and on the 256-row path an item costs 4 to 7 (elsewhere 1)
   const int64_t W = max_tiles * a.n_ntiles;
@@ -784,9 +766,9 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a
   }
   if (BM == 256) {
     if (swiglu)
-      hipLaunchKernelGGL((k_gemm_dl<true>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_dl<true>), dim3(grid), dim3(kGemmThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((k_gemm_dl<false>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_dl<false>), dim3(grid), dim3(kGemmThreads), 0, st, a);
   } else {
     if (swiglu)
       hipLaunchKernelGGL((k_grouped_gemm_bf16<1, 4, 1, 2, true>), dim3(grid), dim3(256), 0, st, a);

@@ -13,7 +13,7 @@ constexpr int kXcds = 8;
 constexpr int kSchedInts = 1 + 2 * (kXcds + 1);
 
 struct GemmArgs {
-  const int4* tiles;         // {group, first row, rows, 0}
+  const int4* tiles;         // per M tile: {group, group's first row, group's rows, group's first tile}
   const int32_t* ntiles;     // device count of valid tiles (schedule entry 0)
   const int32_t* xcd_first;  // this GEMM's 9 XCD boundaries in the schedule
   int E_ffn;
@@ -35,6 +35,7 @@ struct GemmArgs {
   int N_routed, N_shared;  // output columns
   int K_routed, K_shared;
   int n_ntiles;            // N tiles per M tile (set by the launcher)
+  int bm;                  // rows per M tile (set by the launcher)
 };
 
 struct CombineArgs {
