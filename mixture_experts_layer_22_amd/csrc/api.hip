@@ -66,7 +66,7 @@ struct Layout {
   int64_t T, n;
   int NL, Kw, BM, splits;
   int64_t max_tiles;
-  size_t w3, logits, disp, tiles, ntiles, h, hs, idx, gate, counts, offsets, perm, inv, y, sy;
+  size_t logits, disp, tiles, ntiles, h, hs, idx, gate, counts, offsets, perm, inv, y, sy;
   size_t total;
 };
 
@@ -92,7 +92,6 @@ Layout make_layout(const moe_dims* d, int64_t T) {
     off += align_up(bytes);
     return o;
   };
-  L.w3 = take(d->dtype == MOE_BF16 ? (size_t)3 * L.NL * L.Kw * 2 : 0);
   L.logits = take((size_t)L.splits * T * L.NL * 4);
   L.disp = take((size_t)dispatch_scratch_ints(L.n, d->E) * 4);
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
@@ -148,25 +147,18 @@ int32_t check_weights(const moe_dims* d, const moe_weights* w, bool router, bool
 int32_t do_route(const moe_dims* d, const moe_weights* w, const void* x, int64_t T, int32_t* idx,
                  float* gate, void* ws, const Layout& L, hipStream_t st) {
   float* logits = at<float*>(ws, L.logits);
-  const void* W = w->router_w;
-  if (d->dtype == MOE_BF16) {
-    uint16_t* w3 = at<uint16_t*>(ws, L.w3);
-    MOE_TRY(launch_split_router(w->router_w, w3, (int64_t)L.NL * L.Kw, st));
-    W = w3;
-  }
-  const int64_t slice = (int64_t)L.NL * L.Kw;
+  const float* W = w->router_w;
   if (!is_pk(d)) {
-    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, slice, d->E, d->d, logits, d->E, 0,
+    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, d->E, d->d, logits, d->E, 0,
                                  L.splits, st));
     MOE_TRY(launch_select_topk(logits, L.splits, T, d->E, d->E_ffn, d->k, d->ffn_logit_scale,
                                w->router_bias, d->renorm, idx, gate, st));
   } else {
     const int K = L.Kw;
-    const void* Wc = reinterpret_cast<const char*>(W) +
-                     (size_t)d->pk_rows * K * (d->dtype == MOE_BF16 ? 2 : 4);
-    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, slice, d->pk_rows, K, logits, L.NL,
+    const float* Wc = W + (size_t)d->pk_rows * K;
+    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, d->pk_rows, K, logits, L.NL,
                                  0, L.splits, st));
-    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, K, Wc, slice, d->pk_cols, K, logits, L.NL,
+    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, K, Wc, d->pk_cols, K, logits, L.NL,
                                  d->pk_rows, L.splits, st));
     MOE_TRY(launch_select_pk(logits, L.splits, T, d->pk_rows, d->pk_cols, d->pk_k_row,
                              d->pk_k_col, d->k, idx, gate, st));

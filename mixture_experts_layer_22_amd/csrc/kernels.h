@@ -55,10 +55,9 @@ struct CombineArgs {
 };
 
 // router.hip
-hipError_t launch_split_router(const float* W, uint16_t* W3, int64_t n, hipStream_t st);
 int router_splits(int dtype, int64_t T, int NL, int K);
 hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, int x_off,
-                                const void* W, int64_t slice, int NL, int K, float* logits,
+                                const float* W, int NL, int K, float* logits,
                                 int ldl, int col_off, int splits, hipStream_t st);
 hipError_t launch_select_topk(const float* logits, int splits, int64_t T, int E, int E_ffn, int k,
                               float tau, const float* bias, int renorm, int32_t* idx, float* gate,

@@ -12,24 +12,21 @@
 namespace moe {
 
 // ------------------------------------------------------------------------
-// fp32 router weights -> three bf16 slices (hi + mid + lo == w exactly).
+// fp32 router weight -> three bf16 slices (hi + mid + lo == w exactly).
 //
 // hi keeps the top 8 significant bits of w (truncation), mid the next 8 of
 // the exact remainder w - hi, and lo the remaining <= 8 bits, which bf16
 // holds exactly.  A bf16 x times each slice is exact in fp32, so three bf16
 // MFMA passes with fp32 accumulation give an fp32-accurate dot product at
-// matrix-core rate.  Layout: W3[p][n][kk], p = 0..2.
-__global__ void k_split_router(const float* __restrict__ W, uint16_t* __restrict__ W3, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float v = W[i];
-  uint32_t hb = __float_as_uint(v) & 0xffff0000u;
-  float r1 = v - __uint_as_float(hb);
-  uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
-  float r2 = r1 - __uint_as_float(mb);
-  W3[i] = (uint16_t)(hb >> 16);
-  W3[n + i] = (uint16_t)(mb >> 16);
-  W3[2 * n + i] = (uint16_t)(__float_as_uint(r2) >> 16);  // exact: <= 8 bits left
+// matrix-core rate.
+__device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  const uint32_t hb = __float_as_uint(v) & 0xffff0000u;
+  const float r1 = v - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  hi = (uint16_t)(hb >> 16);
+  mid = (uint16_t)(mb >> 16);
+  lo = (uint16_t)(__float_as_uint(r2) >> 16);  // exact: <= 8 bits left
 }
 
 // ------------------------------------------------------------------------
@@ -37,21 +34,22 @@ __global__ void k_split_router(const float* __restrict__ W, uint16_t* __restrict
 //   part[z][t, col_off + n] = x[t, x_off + K_z] . W[n, K_z]   (n < NL)
 // with K_z the z-th of gridDim.z equal K ranges (split K keeps enough
 // blocks busy at small T; the selection kernel adds the partials in order z).
-// bf16 x; W given as three bf16 slices W3[p * slice + n * K + kk].
+// bf16 x; fp32 W [NL, K].
 //
 // Block: 64 tokens x 64 logits; wave w owns tokens 16w..16w+15 and all 64
 // logits (four v_mfma_f32_16x16x32_bf16 tiles).  Per 64-wide K chunk the
-// three weight slices of the block's 64 logits (24 KB) are staged in LDS
-// once and shared by the four waves (double buffered); x fragments go
-// straight from global memory to registers.  K is permuted identically for
-// both operands: lane (r = l%16, q = l/16) takes elements [16q, 16q+16) of
-// the chunk, MFMA step h the half [16q + 8h, +8), so each x row is one
-// 128-byte run.  The three slices accumulate into one fp32 accumulator.
+// block's 64 fp32 weight rows are read once, split into their three bf16
+// slices and staged in LDS (24 KB, double buffered), shared by the four
+// waves; x fragments go straight from global memory to registers.  K is
+// permuted identically for both operands: lane (r = l%16, q = l/16) takes
+// elements [16q, 16q+16) of the chunk, MFMA step h the half [16q + 8h, +8),
+// so each x row is one 128-byte run.  The three slices accumulate into one
+// fp32 accumulator.
 __device__ __forceinline__ int rl_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __global__ __launch_bounds__(256) void k_router_logits_bf16(
     const uint16_t* __restrict__ x, int64_t T, int ldx, int x_off,
-    const uint16_t* __restrict__ W3, int64_t slice, int NL, int K,
+    const float* __restrict__ W, int NL, int K,
     float* __restrict__ logits, int ldl, int col_off, int64_t part_stride) {
   // [buf][slice * 64 + logit][64 K] bf16, 16-byte chunks swizzled
   __shared__ __attribute__((aligned(16))) uint16_t bs[2][3 * 64 * 64];
@@ -65,26 +63,38 @@ __global__ __launch_bounds__(256) void k_router_logits_bf16(
   if (am >= T) am = T - 1;  // clamped rows feed only outputs that are not stored
   const uint16_t* ap = x + am * (int64_t)ldx + x_off + kbeg + q * 16;
 
-  // B loader: 3 * 64 rows x 8 chunks = 1536 chunks, 6 per thread
-  const uint16_t* bsrc[6];
-  int bdst[6];
+  // B loader: 64 rows x 16 float4 = 1024 float4, 4 per thread; float4 i of
+  // this thread is row id/16, K elements 4(id%16) .. +3
+  const float* bsrc[4];
+  int bdst[4];
 #pragma unroll
-  for (int i = 0; i < 6; i++) {
-    const int id = tid + 256 * i;          // 0 .. 1535
-    const int row = id >> 3, ch = id & 7;  // row = slice * 64 + logit
-    const int p = row >> 6, nl = row & 63;
+  for (int i = 0; i < 4; i++) {
+    const int id = tid + 256 * i;
+    const int nl = id >> 4, k4 = (id & 15) * 4;
     const int n = n0 + nl < NL ? n0 + nl : NL - 1;
-    bsrc[i] = W3 + p * slice + (int64_t)n * K + kbeg + ch * 8;
-    bdst[i] = row * 64 + ((ch ^ rl_swz(row)) * 8);
+    bsrc[i] = W + (int64_t)n * K + kbeg + k4;
+    bdst[i] = nl * 64 + (((k4 >> 3) ^ rl_swz(nl)) * 8) + (k4 & 7);  // slice 0 position
   }
-  u32x4 breg[6];
+  f32x4 breg[4];
   auto bload = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < 6; i++) breg[i] = *reinterpret_cast<const u32x4*>(bsrc[i] + c * 64);
+    for (int i = 0; i < 4; i++) breg[i] = *reinterpret_cast<const f32x4*>(bsrc[i] + c * 64);
   };
   auto bstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 6; i++) *reinterpret_cast<u32x4*>(&bs[buf][bdst[i]]) = breg[i];
+    for (int i = 0; i < 4; i++) {
+      uint16_t h[4], m[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) split3(breg[i][e], h[e], m[e], l[e]);
+      auto pack = [](const uint16_t (&v)[4]) {
+        return make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                          (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+      };
+      // rows of slice p are p*64 + nl: same swizzle, offset p * 64 rows
+      *reinterpret_cast<uint2*>(&bs[buf][bdst[i]]) = pack(h);
+      *reinterpret_cast<uint2*>(&bs[buf][64 * 64 + bdst[i]]) = pack(m);
+      *reinterpret_cast<uint2*>(&bs[buf][2 * 64 * 64 + bdst[i]]) = pack(l);
+    }
   };
 
   f32x4 acc[4];
@@ -312,12 +322,6 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
 // ------------------------------------------------------------------------
 // launchers
 
-hipError_t launch_split_router(const float* W, uint16_t* W3, int64_t n, hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_split_router, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, W, W3, n);
-  return hipGetLastError();
-}
-
 int router_splits(int dtype, int64_t T, int NL, int K) {
   if (dtype != MOE_BF16) return 1;
   const int64_t blocks = cdiv(T, 64) * cdiv(NL, 64);
@@ -327,18 +331,16 @@ int router_splits(int dtype, int64_t T, int NL, int K) {
 }
 
 hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, int x_off,
-                                const void* W, int64_t slice, int NL, int K, float* logits,
+                                const float* W, int NL, int K, float* logits,
                                 int ldl, int col_off, int splits, hipStream_t st) {
   if (T == 0 || NL == 0) return hipSuccess;
   if (dtype == MOE_BF16) {
     dim3 grid((unsigned)cdiv(T, 64), (unsigned)cdiv(NL, 64), (unsigned)splits);
     hipLaunchKernelGGL(k_router_logits_bf16, grid, dim3(256), 0, st, (const uint16_t*)x, T, ldx,
-                       x_off, (const uint16_t*)W, slice, NL, K, logits, ldl, col_off,
-                       (int64_t)T * ldl);
+                       x_off, W, NL, K, logits, ldl, col_off, (int64_t)T * ldl);
   } else {
     hipLaunchKernelGGL(k_router_logits_f32, dim3((unsigned)cdiv(T * NL, 256)), dim3(256), 0, st,
-                       (const float*)x, T, ldx, x_off, (const float*)W, NL, K, logits, ldl,
-                       col_off);
+                       (const float*)x, T, ldx, x_off, W, NL, K, logits, ldl, col_off);
   }
   return hipGetLastError();
 }
