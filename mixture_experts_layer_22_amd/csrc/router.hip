@@ -222,12 +222,95 @@ __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ l
 }
 
 // ------------------------------------------------------------------------
+// Wave-wide selection helpers.  A wave holds up to 64 V (key, id) pairs, V
+// per lane (slot i of lane l).  Keys are fp32 scores mapped to uint32 so
+// that unsigned order is score order; ids are unique.  Rank order is (key
+// descending, id ascending); NaN scores are not supported.
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = f == 0.f ? 0u : __float_as_uint(f);  // -0 ranks as +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Marks in sel (bit i = slot i) the K best valid pairs: the K-th largest
+// key th is found bit by bit (a key prefix is kept while at least K keys
+// reach it), every key above th is taken, and the keys equal to th are
+// taken by ascending id until K are.
+template <int V>
+__device__ __forceinline__ uint32_t wave_select(const uint32_t (&key)[V], const int (&id)[V],
+                                                uint32_t valid, int K) {
+  uint32_t th = 0;
+  for (int b = 31; b >= 0; b--) {
+    const uint32_t cand = th | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < V; i++) cnt += __popcll(__ballot(((valid >> i) & 1u) && key[i] >= cand));
+    if (cnt >= K) th = cand;
+  }
+  uint32_t sel = 0, eq = 0;
+  int gt = 0, neq = 0;
+#pragma unroll
+  for (int i = 0; i < V; i++) {
+    const bool v = (valid >> i) & 1u;
+    if (v && key[i] > th) sel |= 1u << i;
+    if (v && key[i] == th) eq |= 1u << i;
+    gt += __popcll(__ballot(v && key[i] > th));
+    neq += __popcll(__ballot(v && key[i] == th));
+  }
+  int need = K - gt;
+  if (need >= neq) return sel | eq;
+  // more ties than places: smallest ids first
+  for (; need > 0; need--) {
+    int best = 0x7fffffff, slot = -1;
+#pragma unroll
+    for (int i = 0; i < V; i++)
+      if (((eq >> i) & 1u) && id[i] < best) { best = id[i]; slot = i; }
+    const int m = wave_reduce_dpp(best, [](int a, int b) { return a < b ? a : b; });
+    if (slot >= 0 && best == m) {
+      sel |= 1u << slot;
+      eq &= ~(1u << slot);
+    }
+  }
+  return sel;
+}
+
+// Position of each selected pair in [0, K): slots in order, lanes in order.
+template <int V>
+__device__ __forceinline__ void wave_positions(uint32_t sel, int (&pos)[V]) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < V; i++) {
+    const uint64_t m = __ballot((sel >> i) & 1u);
+    pos[i] = base + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+    base += __popcll(m);
+  }
+}
+
+// Sorts one (key, id) pair per lane across the wave, best first (bitonic
+// network; pad lanes with key 0, id INT_MAX).
+__device__ __forceinline__ void wave_sort(uint32_t& key, int& id) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      const uint32_t ok = __shfl_xor(key, stride, kWave);
+      const int oi = __shfl_xor(id, stride, kWave);
+      const bool first = key > ok || (key == ok && id < oi);
+      const bool keep = (((lane & stride) == 0) == ((lane & size) == 0)) ? first : !first;
+      if (!keep) { key = ok; id = oi; }
+    }
+}
+
+// ------------------------------------------------------------------------
 // Cartesian-product selection, one wave per token.
 //   scores: [T, rows + cols] (row scores first).
 //   1. top-krow rows, top-kcol columns by (-score, index);
 //   2. candidates (a, b): sigma = fl32(s_r + s_c), id = row * cols + col;
 //   3. top-k candidates by (-sigma, id); gates = softmax over the k sigmas.
-// V = values per lane (max(rows, cols, krow*kcol) <= 64 V); krow, kcol <= 64.
+// V = values per lane (max(rows, cols, krow*kcol) <= 64 V); krow, kcol, k
+// <= 64.
 template <int V>
 __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ scores, int nparts,
                                                   int64_t part_stride, int64_t T,
@@ -236,86 +319,92 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
                                                   float* __restrict__ gate_out) {
   __shared__ float sel_val[4][2][64];
   __shared__ int sel_idx[4][2][64];
+  __shared__ uint32_t top_key[4][64];
+  __shared__ int top_id[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
   const float* srow = scores + t * (int64_t)(rows + cols);
-  // steps 1: rows then columns
+  // step 1: rows then columns
   for (int side = 0; side < 2; side++) {
     const int n = side ? cols : rows;
     const int kk = side ? kcol : krow;
     const float* s = srow + (side ? rows : 0);
     float v[V];
+    uint32_t key[V];
+    int id[V];
+    uint32_t valid = 0;
 #pragma unroll
     for (int i = 0; i < V; i++) {
-      int e = lane + 64 * i;
+      const int e = lane + 64 * i;
       float sc = -INFINITY;
       if (e < n) {
         sc = s[e];
         for (int z = 1; z < nparts; z++) sc += s[z * part_stride + e];
+        valid |= 1u << i;
       }
       v[i] = sc;
+      key[i] = order_key(sc);
+      id[i] = e;
     }
-    uint32_t taken = 0;
-    for (int j = 0; j < kk; j++) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+    const uint32_t sel = wave_select<V>(key, id, valid, kk);
+    int pos[V];
+    wave_positions<V>(sel, pos);
 #pragma unroll
-      for (int i = 0; i < V; i++) {
-        int e = lane + 64 * i;
-        bool ok = e < n && !((taken >> i) & 1u);
-        if (ok && (v[i] > bv || bi == 0x7fffffff)) { bv = v[i]; bi = e; }
+    for (int i = 0; i < V; i++)
+      if ((sel >> i) & 1u) {
+        sel_val[wave][side][pos[i]] = v[i];
+        sel_idx[wave][side][pos[i]] = id[i];
       }
-      wave_argmax(bv, bi);
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) { sel_val[wave][side][j] = bv; sel_idx[wave][side][j] = bi; }
-    }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   // step 2: candidate scores
   const int nc = krow * kcol;
   float v[V];
+  uint32_t key[V];
   int id[V];
+  uint32_t valid = 0;
 #pragma unroll
   for (int i = 0; i < V; i++) {
-    int c = lane + 64 * i;
+    const int c = lane + 64 * i;
     if (c < nc) {
-      int a = c / kcol, b = c - a * kcol;
+      const int a = c / kcol, b = c - a * kcol;
       v[i] = sel_val[wave][0][a] + sel_val[wave][1][b];
       id[i] = sel_idx[wave][0][a] * cols + sel_idx[wave][1][b];
+      valid |= 1u << i;
     } else {
       v[i] = -INFINITY;
       id[i] = 0x7fffffff;
     }
+    key[i] = order_key(v[i]);
   }
-  // step 3: top-k candidates
-  uint32_t taken = 0;
-  float top = 0.f, my_val = 0.f;
-  int my_id = 0;
-  float gsum = 0.f;
-  for (int j = 0; j < k; j++) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff, bslot = 0;
+  // step 3: the k best candidates, gathered in lanes 0..k-1 and sorted
+  const uint32_t sel = wave_select<V>(key, id, valid, k);
+  int pos[V];
+  wave_positions<V>(sel, pos);
 #pragma unroll
-    for (int i = 0; i < V; i++) {
-      bool ok = (lane + 64 * i) < nc && !((taken >> i) & 1u);
-      if (ok && (v[i] > bv || (v[i] == bv && id[i] < bi))) { bv = v[i]; bi = id[i]; bslot = i; }
+  for (int i = 0; i < V; i++)
+    if ((sel >> i) & 1u) {
+      top_key[wave][pos[i]] = key[i];
+      top_id[wave][pos[i]] = id[i];
     }
-    int owner_key = bi;
-    wave_argmax(bv, bi);
-    if (owner_key == bi && bi != 0x7fffffff) {
-      // the lane holding the winner marks it (ids are unique)
-      taken |= 1u << bslot;
-    }
-    if (j == 0) top = bv;
-    float e = __expf(bv - top);
-    gsum += e;
-    if (lane == j) { my_val = e; my_id = bi; }
-  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  uint32_t mk = lane < k ? top_key[wave][lane] : 0u;
+  int mi = lane < k ? top_id[wave][lane] : 0x7fffffff;
+  wave_sort(mk, mi);
+  // back to fp32 scores; gates = softmax over the k (the first is the max)
+  const uint32_t bits = (mk & 0x80000000u) ? (mk & 0x7fffffffu) : ~mk;
+  const float sv = __uint_as_float(bits);
+  const float top = __shfl(sv, 0, kWave);
+  const float e = lane < k ? __expf(sv - top) : 0.f;
+  // the sum in rank order, as the selection loop did it
+  float gsum = 0.f;
+  for (int j = 0; j < k; j++) gsum += __shfl(e, j, kWave);
   if (lane < k) {
-    idx_out[t * k + lane] = my_id;
-    gate_out[t * k + lane] = my_val / gsum;
+    idx_out[t * k + lane] = mi;
+    gate_out[t * k + lane] = e / gsum;
   }
 }
 
