@@ -166,10 +166,27 @@ int32_t do_route(const moe_dims* d, const moe_weights* w, const void* x, int64_t
   return MOE_OK;
 }
 
+// The expert GEMMs' tile list build for these dims (tiles == nullptr when
+// the layer has no GEMM).
+TileBuild tile_build(const moe_dims* d, int64_t T, void* ws, const Layout& L) {
+  TileBuild tb;
+  const int E_groups = is_pk(d) ? 0 : d->E_ffn;
+  const int N1 = E_groups ? d->f : d->f_shared;
+  tb.tiles = (E_groups > 0 || d->n_shared > 0) ? at<int4*>(ws, L.tiles) : nullptr;
+  tb.sched = at<int32_t*>(ws, L.ntiles);
+  tb.E_ffn = E_groups;
+  tb.n_shared = d->n_shared;
+  tb.BM = L.BM;
+  tb.nn1 = gemm_n_ntiles(d->dtype, true, d->n_shared && d->f_shared > N1 ? d->f_shared : N1);
+  tb.nn2 = gemm_n_ntiles(d->dtype, false, d->d);
+  tb.T = T;
+  return tb;
+}
+
 int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64_t T,
                    const int32_t* idx, const int32_t* perm, const int32_t* offsets, void* y,
                    void* shared_y, void* ws, const Layout& L, hipStream_t st,
-                   void* const* ev = nullptr) {
+                   void* const* ev = nullptr, bool tiles_built = false) {
   auto mark = [&](int i) -> hipError_t {
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
   };
@@ -177,11 +194,10 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   const bool gemms = E_groups > 0 || d->n_shared > 0;
   int4* tiles = at<int4*>(ws, L.tiles);
   int32_t* ntiles = at<int32_t*>(ws, L.ntiles);
-  const int N1 = E_groups ? d->f : d->f_shared;
-  const int nn1 = gemm_n_ntiles(d->dtype, true, d->n_shared && d->f_shared > N1 ? d->f_shared : N1);
-  const int nn2 = gemm_n_ntiles(d->dtype, false, d->d);
-  if (gemms)
-    MOE_TRY(launch_build_tiles(offsets, E_groups, d->n_shared, T, L.BM, nn1, nn2, tiles, ntiles, st));
+  const TileBuild tb = tile_build(d, T, ws, L);
+  if (gemms && !tiles_built)
+    MOE_TRY(launch_build_tiles(offsets, E_groups, d->n_shared, T, L.BM, tb.nn1, tb.nn2, tiles,
+                               ntiles, st));
   MOE_TRY(mark(3));
   if (is_pk(d)) {
     MOE_TRY(launch_atomic_h(d->dtype, x, w->atom_u, idx, perm, L.n, d->k, d->d, (float*)y, st));
@@ -386,10 +402,14 @@ int32_t moe_forward_traced(const moe_dims* dims, const moe_weights* w, const voi
   MOE_TRY(mark(0));
   if ((s = do_route(dims, w, x, T, idx, gate, ws, L, st)) != MOE_OK) return s;
   MOE_TRY(mark(1));
+  // a single-pass dispatch also builds the expert GEMMs' tile list
+  const TileBuild tb = tile_build(dims, T, ws, L);
+  const bool fused = tb.tiles && dispatch_builds_tiles(L.n, dims->E);
   MOE_TRY(launch_dispatch(idx, L.n, dims->E, counts, offsets, perm, inv,
-                          at<int32_t*>(ws, L.disp), st));
+                          at<int32_t*>(ws, L.disp), st, fused ? &tb : nullptr));
   MOE_TRY(mark(2));
-  if ((s = do_experts(dims, w, x, T, idx, perm, offsets, y, sy, ws, L, st, events)) != MOE_OK)
+  if ((s = do_experts(dims, w, x, T, idx, perm, offsets, y, sy, ws, L, st, events, fused)) !=
+      MOE_OK)
     return s;
   MOE_TRY(mark(5));
   if ((s = do_combine(dims, w, x, T, idx, gate, inv, y, sy, out, st)) != MOE_OK) return s;

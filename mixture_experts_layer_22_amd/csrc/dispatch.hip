@@ -14,6 +14,7 @@
 // passes).  The only atomics are integer adds on LDS counters, whose results
 // do not depend on order, so the output is bit-exact and deterministic.
 #include "kernels.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -68,10 +69,11 @@ __global__ __launch_bounds__(256) void k_digit_scan(int32_t* __restrict__ hist, 
 
 // Single-pass dispatch (E <= 256): exclusive scan of the digit-major tile
 // histogram in place, and from it the expert offsets (the scanned value at
-// (e, tile 0)) and counts.
+// (e, tile 0)) and counts; then, when asked, the expert GEMMs' tile list.
 __global__ __launch_bounds__(1024) void k_dispatch_scan(int32_t* hist, int64_t len, int nb, int E,
                                                         int64_t n, int32_t* __restrict__ counts,
-                                                        int32_t* __restrict__ offsets) {
+                                                        int32_t* __restrict__ offsets,
+                                                        TileBuild tb) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   const int64_t per = (len + 1023) / 1024;
@@ -97,6 +99,9 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int32_t* hist, int64_t l
   if (tid == 0) offsets[E] = (int32_t)n;
   __syncthreads();
   for (int e = tid; e < E; e += 1024) counts[e] = offsets[e + 1] - offsets[e];
+  if (tb.tiles)
+    build_tile_list(offsets, tb.E_ffn, tb.n_shared, tb.T, tb.BM, tb.nn1, tb.nn2, tb.tiles,
+                    tb.sched);
 }
 
 __device__ __forceinline__ int radix_digit(const int32_t* idx, int32_t task, int shift, int mask) {
@@ -227,9 +232,11 @@ int64_t dispatch_scratch_ints(int64_t n, int E) {
   return 256 * nb + (passes > 1 ? 256 + n : 0);
 }
 
+bool dispatch_builds_tiles(int64_t n, int E) { return n > 0 && E <= 256; }
+
 hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* scratch,
-                           hipStream_t st) {
+                           hipStream_t st, const TileBuild* tb) {
   int bits = 0;
   while ((1ll << bits) < E) bits++;
   if (bits == 0) bits = 1;  // one expert: a pass on a constant digit keeps task order
@@ -246,8 +253,10 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     int32_t* hist = scratch;
     hipLaunchKernelGGL(k_radix_hist<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
                        (const int32_t*)nullptr, n, 0, bits, hist, nb);
+    TileBuild none;
+    none.tiles = nullptr;
     hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, st, hist,
-                       (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets);
+                       (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets, tb ? *tb : none);
     hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
                        (const int32_t*)nullptr, n, 0, bits, hist, (const int32_t*)nullptr, nb,
                        perm, inv_perm);

@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -616,106 +617,14 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
 }
 
 // ------------------------------------------------------------------------
-// Tile list: routed experts e < E_ffn get ceil(count_e / BM) tiles of
-// sorted positions; shared expert s gets ceil(T / BM) tiles of tokens.  Each
-// tile's descriptor names its whole group (see tile_ctx).
-//
-// Then the XCD schedule of both GEMMs.  The expert GEMMs are bound by the
-// rate at which a CU pulls operand bytes from L2, and a 256-row-path item
-// reads its 256 weight rows whatever its height: timed per block, an item
-// costs about a fixed 3 plus 1 per 64 rows of its variant (4 for 64 rows,
-// 7 for 256).  Tiles of the other paths have one size and cost 1.  XCD x
-// starts at the first item whose cost prefix reaches x/8 of the total.
-// Single block; E_ffn <= 1024.
-__device__ __forceinline__ int tile_cost(int BM, int rows) {
-  return BM == 256 ? (rows + 63) / 64 + 3 : 1;
-}
-
-// Tiles [first, first + n) of one group, all of `full` rows but the last of
-// `last` rows, starting at cost prefix P: writes every XCD boundary that
-// falls in them.  A target t lands in tile i (prefix Pi, cost c) when
-// Pi*nn < t <= (Pi+c)*nn, at item i*nn + ceil((t - Pi*nn) / c).
-__device__ __forceinline__ void place_targets(int first, int n, int full, int last, int BM,
-                                              int64_t P, int64_t total, int nn1, int nn2,
-                                              int32_t* sched) {
-  const uint32_t cf = tile_cost(BM, full), cl = tile_cost(BM, last);
-  // rolled loops: the kernel runs once per layer call on a cold instruction
-  // cache, so its code must stay small; offsets inside one group fit in 32
-  // bits, so the divisions are 32-bit
-#pragma unroll 1
-  for (int g = 0; g < 2; g++) {
-    const uint32_t nn = g == 0 ? nn1 : nn2;
-    const int64_t lo = P * nn, hi = (P + (int64_t)(n - 1) * cf + cl) * nn;
-#pragma unroll 1
-    for (int x = 1; x < kXcds; x++) {
-      const int64_t tgt = (x * total * nn + kXcds - 1) / kXcds;
-      if (tgt <= lo || tgt > hi) continue;
-      // full tiles first, then the last one
-      const uint32_t d = (uint32_t)(tgt - lo);  // in [1, hi - lo]
-      uint32_t i = (d - 1) / (cf * nn);
-      if (i > (uint32_t)(n - 1)) i = n - 1;
-      const uint32_t c = i == (uint32_t)(n - 1) ? cl : cf;
-      const uint32_t r = d - i * cf * nn;       // target minus the tile's prefix, >= 1
-      sched[1 + g * (kXcds + 1) + x] = (int32_t)((first + i) * nn + (r + c - 1) / c);
-    }
-  }
-}
-
+// Tile list and XCD schedule (the builder itself is in tiles.h, shared with
+// the dispatch scan, which builds them in the same launch for a forward).
 __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ offsets,
                                                       int E_ffn, int n_shared, int64_t T, int BM,
                                                       int nn1, int nn2,
                                                       int4* __restrict__ tiles,
                                                       int32_t* __restrict__ sched) {
-  __shared__ int32_t pre[1024];
-  __shared__ int32_t prc[1024];
-  const int e = threadIdx.x;
-  const int cnt = e < E_ffn ? offsets[e + 1] - offsets[e] : 0;
-  const int nt = (cnt + BM - 1) / BM;
-  const int last = cnt - (nt - 1) * BM;
-  const int ce = nt ? (nt - 1) * tile_cost(BM, BM) + tile_cost(BM, last) : 0;
-  pre[e] = nt;
-  prc[e] = ce;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = e >= o ? pre[e - o] : 0;
-    const int w = e >= o ? prc[e - o] : 0;
-    __syncthreads();
-    pre[e] += v;
-    prc[e] += w;
-    __syncthreads();
-  }
-  const int start = pre[e] - nt;
-  const int routed_total = pre[1023];
-  const int64_t routed_cost = prc[1023];
-  if (e < E_ffn) {
-    const int base = offsets[e];
-    for (int i = 0; i < nt; i++) tiles[start + i] = make_int4(e, base, cnt, start);
-  }
-  const int per_shared = (int)((T + BM - 1) / BM);
-  const int shared_last = (int)(T - (int64_t)(per_shared - 1) * BM);
-  for (int j = e; j < n_shared * per_shared; j += 1024) {
-    const int s = j / per_shared;
-    tiles[routed_total + j] = make_int4(E_ffn + s, 0, (int)T, routed_total + s * per_shared);
-  }
-  const int ntot = routed_total + n_shared * per_shared;
-  const int64_t cs = per_shared ? (int64_t)(per_shared - 1) * tile_cost(BM, BM) +
-                                      tile_cost(BM, shared_last) : 0;
-  const int64_t total = routed_cost + n_shared * cs;
-
-  if (e == 0) {
-    sched[0] = ntot;
-    for (int g = 0; g < 2; g++) {
-      const int nn = g == 0 ? nn1 : nn2;
-      for (int x = 0; x < kXcds; x++) sched[1 + g * (kXcds + 1) + x] = 0;  // targets of an empty list
-      sched[1 + g * (kXcds + 1) + kXcds] = ntot * nn;
-    }
-  }
-  __syncthreads();
-  if (e < E_ffn && nt > 0)
-    place_targets(start, nt, BM, last, BM, prc[e] - ce, total, nn1, nn2, sched);
-  if (e < n_shared && per_shared > 0)
-    place_targets(routed_total + e * per_shared, per_shared, BM, shared_last, BM,
-                  routed_cost + e * cs, total, nn1, nn2, sched);
+  build_tile_list(offsets, E_ffn, n_shared, T, BM, nn1, nn2, tiles, sched);
 }
 
 // ------------------------------------------------------------------------

@@ -67,9 +67,20 @@ hipError_t launch_select_pk(const float* scores, int splits, int64_t T, int rows
 
 // dispatch.hip
 int64_t dispatch_scratch_ints(int64_t n, int E);
+// whether launch_dispatch can build a tile list (it does when given one)
+bool dispatch_builds_tiles(int64_t n, int E);
+// Optional build of the expert GEMMs' tile list inside the dispatch scan
+// (single-pass dispatch only; tiles == nullptr: none).
+struct TileBuild {
+  int4* tiles;
+  int32_t* sched;
+  int E_ffn, n_shared, BM, nn1, nn2;
+  int64_t T;
+};
 hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* scratch,
-                           hipStream_t st);
+                           hipStream_t st,
+                           const TileBuild* tb = nullptr);
 
 // gemm.hip
 int gemm_tile_rows(int dtype, int64_t tasks, int E_ffn);

@@ -1,0 +1,121 @@
+// Tile list of the expert GEMMs and its XCD schedule, built by one block of
+// 1024 threads (the tile builder kernel, or the dispatch scan of a forward).
+#pragma once
+
+#include "kernels.h"
+
+namespace moe {
+
+// Tile list: routed experts e < E_ffn get ceil(count_e / BM) tiles of
+// sorted positions; shared expert s gets ceil(T / BM) tiles of tokens.  Each
+// tile's descriptor names its whole group: {group, first row, rows, first
+// tile}.
+//
+// Then the XCD schedule of both GEMMs.  The expert GEMMs are bound by the
+// rate at which a CU pulls operand bytes from L2, and a 256-row-path item
+// reads its 256 weight rows whatever its height: timed per block, an item
+// costs about a fixed 3 plus 1 per 64 rows of its variant (4 for 64 rows,
+// 7 for 256).  Tiles of the other paths have one size and cost 1.  XCD x
+// starts at the first item whose cost prefix reaches x/8 of the total.
+// Single block; E_ffn <= 1024.
+__device__ __forceinline__ int tile_cost(int BM, int rows) {
+  return BM == 256 ? (rows + 63) / 64 + 3 : 1;
+}
+
+// Tiles [first, first + n) of one group, all of `full` rows but the last of
+// `last` rows, starting at cost prefix P: writes every XCD boundary that
+// falls in them.  A target t lands in tile i (prefix Pi, cost c) when
+// Pi*nn < t <= (Pi+c)*nn, at item i*nn + ceil((t - Pi*nn) / c).
+__device__ __forceinline__ void place_targets(int first, int n, int full, int last, int BM,
+                                              int64_t P, int64_t total, int nn1, int nn2,
+                                              int32_t* sched) {
+  const uint32_t cf = tile_cost(BM, full), cl = tile_cost(BM, last);
+  // rolled loops: the kernel runs once per layer call on a cold instruction
+  // cache, so its code must stay small; offsets inside one group fit in 32
+  // bits, so the divisions are 32-bit
+#pragma unroll 1
+  for (int g = 0; g < 2; g++) {
+    const uint32_t nn = g == 0 ? nn1 : nn2;
+    const int64_t lo = P * nn, hi = (P + (int64_t)(n - 1) * cf + cl) * nn;
+#pragma unroll 1
+    for (int x = 1; x < kXcds; x++) {
+      const int64_t tgt = (x * total * nn + kXcds - 1) / kXcds;
+      if (tgt <= lo || tgt > hi) continue;
+      // full tiles first, then the last one
+      const uint32_t d = (uint32_t)(tgt - lo);  // in [1, hi - lo]
+      uint32_t i = (d - 1) / (cf * nn);
+      if (i > (uint32_t)(n - 1)) i = n - 1;
+      const uint32_t c = i == (uint32_t)(n - 1) ? cl : cf;
+      const uint32_t r = d - i * cf * nn;       // target minus the tile's prefix, >= 1
+      sched[1 + g * (kXcds + 1) + x] = (int32_t)((first + i) * nn + (r + c - 1) / c);
+    }
+  }
+}
+
+// Builds the tile list and the schedule with the calling block's 1024
+// threads (offsets must be visible to the whole block).
+__device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offsets, int E_ffn,
+                                                int n_shared, int64_t T, int BM, int nn1, int nn2,
+                                                int4* __restrict__ tiles,
+                                                int32_t* __restrict__ sched) {
+  __shared__ int32_t wtot[2][16];
+  const int e = threadIdx.x;
+  const int cnt = e < E_ffn ? offsets[e + 1] - offsets[e] : 0;
+  const int nt = (cnt + BM - 1) / BM;
+  const int last = cnt - (nt - 1) * BM;
+  const int ce = nt ? (nt - 1) * tile_cost(BM, BM) + tile_cost(BM, last) : 0;
+  // inclusive scans of (nt, ce) over the 1024 threads: within each wave by
+  // shuffles, then across the 16 wave totals
+  const int lane = e & 63, wv = e >> 6;
+  int sn = nt, sc = ce;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(sn, o, 64), b = __shfl_up(sc, o, 64);
+    if (lane >= o) { sn += a; sc += b; }
+  }
+  if (lane == 63) { wtot[0][wv] = sn; wtot[1][wv] = sc; }
+  __syncthreads();
+  int bn = 0, bc = 0, tn = 0, tc = 0;
+#pragma unroll
+  for (int w = 0; w < 16; w++) {
+    const int a = wtot[0][w], b = wtot[1][w];
+    if (w < wv) { bn += a; bc += b; }
+    tn += a;
+    tc += b;
+  }
+  const int start = bn + sn - nt;              // exclusive prefix of tile counts
+  const int cstart = bc + sc - ce;             // exclusive prefix of tile costs
+  const int routed_total = tn;
+  const int64_t routed_cost = tc;
+  if (e < E_ffn) {
+    const int base = offsets[e];
+    for (int i = 0; i < nt; i++) tiles[start + i] = make_int4(e, base, cnt, start);
+  }
+  const int per_shared = (int)((T + BM - 1) / BM);
+  const int shared_last = (int)(T - (int64_t)(per_shared - 1) * BM);
+  for (int j = e; j < n_shared * per_shared; j += 1024) {
+    const int s = j / per_shared;
+    tiles[routed_total + j] = make_int4(E_ffn + s, 0, (int)T, routed_total + s * per_shared);
+  }
+  const int ntot = routed_total + n_shared * per_shared;
+  const int64_t cs = per_shared ? (int64_t)(per_shared - 1) * tile_cost(BM, BM) +
+                                      tile_cost(BM, shared_last) : 0;
+  const int64_t total = routed_cost + n_shared * cs;
+
+  if (e == 0) {
+    sched[0] = ntot;
+    for (int g = 0; g < 2; g++) {
+      const int nn = g == 0 ? nn1 : nn2;
+      for (int x = 0; x < kXcds; x++) sched[1 + g * (kXcds + 1) + x] = 0;  // targets of an empty list
+      sched[1 + g * (kXcds + 1) + kXcds] = ntot * nn;
+    }
+  }
+  __syncthreads();
+  if (e < E_ffn && nt > 0)
+    place_targets(start, nt, BM, last, BM, cstart, total, nn1, nn2, sched);
+  if (e < n_shared && per_shared > 0)
+    place_targets(routed_total + e * per_shared, per_shared, BM, shared_last, BM,
+                  routed_cost + e * cs, total, nn1, nn2, sched);
+}
+
+}  // namespace moe
