@@ -99,6 +99,122 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
                       f"({done} tokens, {el:.1f} s), full layer per batch"}
 
 
+TAUS = (1.0, 0.75, 0.5, 0.25, 0.1)
+
+
+def tau_sweep(args, torch, B, I):
+    """MoE++ "Measured effects": a smaller tau sends more tokens to the zero-
+    computation experts, so the FFN experts' share of the tasks and the expert
+    stage's time fall.  Same weights and tokens at every tau."""
+    base = I.CONFIGS["moepp"]
+    inp = I.make_inputs(base)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    x = B.to_device(inp["x"], dev)
+    T = base.T
+    stream = torch.cuda.current_stream()
+    ref_us = None
+    for tau in TAUS:
+        cfg = base.replace(tau=tau)
+        layer = B.MoELayer(cfg, inp, dev)
+        out = torch.empty((T, cfg.d), dtype=layer.act_dtype, device=dev)
+        ws = layer.workspace(T)
+        idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+        gate = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            B.moe_forward(layer.dims, layer.weights, x, T, out, ws, idx, gate, stream)
+        torch.cuda.synchronize()
+        counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.E)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            B.moe_forward(layer.dims, layer.weights, x, T, out, ws, idx, gate, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        n_tr = max(1, min(args.steps, 10))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_PHASES + 1)]
+               for _ in range(n_tr)]
+        for row in evs:
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for i in range(n_tr):
+            B.moe_forward_traced(layer.dims, layer.weights, x, T, out, ws, evs[i], idx, gate,
+                                 stream)
+        torch.cuda.synchronize()
+        ph = {name: 1e3 * float(np.mean([evs[i][p].elapsed_time(evs[i][p + 1])
+                                          for i in range(n_tr)]))
+              for p, name in enumerate(B.PHASES)}
+        expert_us = ph["expert1"] + ph["expert2"]
+        if ref_us is None:
+            ref_us = expert_us
+        print(json.dumps({
+            "metric": "moepp_tau_sweep", "tau": tau,
+            "ffn_task_share": float(counts[:cfg.E_ffn].sum()) / (T * cfg.k),
+            "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "expert_stage_us": expert_us,
+            "expert_stage_speedup_vs_tau1": ref_us / expert_us,
+            "phases_us": ph, "config": {"workload": "moepp", "T": T, "steps": args.steps}}),
+            flush=True)
+        del layer, ws, out
+
+
+def token_centric_ablation(args, torch, B, I):
+    """OmniMoE sec. 2.2 / sec. 4: expert-centric scheduling (dispatch, then
+    per-expert activations, then the gathered down projection) against the
+    token-centric form (each token gathers its own experts' vectors).  Both
+    start from the same routing; the times compared are everything after it."""
+    cfg = I.CONFIGS["atomic-pk"]
+    inp = I.make_inputs(cfg)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    layer = B.MoELayer(cfg, inp, dev)
+    x = B.to_device(inp["x"], dev)
+    T = cfg.T
+    stream = torch.cuda.current_stream()
+    out = torch.empty((T, cfg.d), dtype=layer.act_dtype, device=dev)
+    ws = layer.workspace(T)
+    idx, gate = layer.route(x)
+    for _ in range(args.warmup):
+        B.moe_forward(layer.dims, layer.weights, x, T, out, ws, stream=stream)
+        B.moe_ablation_atomic_token_centric(layer.dims, layer.weights, x, T, idx, gate, out,
+                                            stream)
+    torch.cuda.synchronize()
+    # expert-centric: phases after routing, from traced forwards
+    n_tr = max(1, min(args.steps, 20))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_PHASES + 1)]
+           for _ in range(n_tr)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(n_tr):
+        B.moe_forward_traced(layer.dims, layer.weights, x, T, out, ws, evs[i], stream=stream)
+    torch.cuda.synchronize()
+    ph = {name: 1e3 * float(np.mean([evs[i][p].elapsed_time(evs[i][p + 1])
+                                      for i in range(n_tr)]))
+          for p, name in enumerate(B.PHASES)}
+    ec_us = sum(v for k, v in ph.items() if k != "route")
+    # token-centric: the one kernel
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        B.moe_ablation_atomic_token_centric(layer.dims, layer.weights, x, T, idx, gate, out,
+                                            stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tc_us = 1e3 * e0.elapsed_time(e1) / args.steps
+    print(json.dumps({
+        "metric": "atomic_expert_centric_vs_token_centric",
+        "expert_centric_us": ec_us, "expert_centric_phases_us": ph,
+        "token_centric_us": tc_us, "token_over_expert_time": tc_us / ec_us,
+        "config": {"workload": cfg.name, "T": T, "d": cfg.d, "N": cfg.E, "k": cfg.k,
+                   "steps": args.steps}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +224,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer three times (counter calibration)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="atomic layer: expert-centric library path against the token-centric "
+                         "ablation kernel, one JSON line (not the bench line)")
+    ap.add_argument("--tau-sweep", action="store_true",
+                    help="MoE++ layer at several tau: one JSON line per tau with the FFN task "
+                         "share and the layer / expert-stage times (not the bench line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -126,6 +248,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+        return
+
+    if args.tau_sweep:
+        tau_sweep(args, torch, B, I)
+        return
+    if args.ablation:
+        token_centric_ablation(args, torch, B, I)
         return
 
     cfg = I.CONFIGS[args.workload]

@@ -212,6 +212,38 @@ def moe_forward_traced(dims, w: DeviceWeights, x, T, out, ws, events, topk_idx=N
                                      _stream(stream), arr), "moe_forward_traced")
 
 
+# ---------------------------------------------------------------- ablation library
+
+ABL_PATH = os.path.join(HERE, "libmoe_ablation.so")
+ABL_EXPORTED = ["moe_ablation_atomic_token_centric"]
+_abl = None
+
+
+def load_ablation(path: str = ABL_PATH) -> ctypes.CDLL:
+    """Load the ablation library (include/moe_ablation.h).  Raises if it has
+    not been built."""
+    global _abl
+    if _abl is not None:
+        return _abl
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m mixture_experts_layer_22_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.moe_ablation_atomic_token_centric.restype = ctypes.c_int32
+    lib.moe_ablation_atomic_token_centric.argtypes = [
+        ctypes.POINTER(MoeDims), ctypes.POINTER(MoeWeights), P, ctypes.c_int64, P, P, P, P]
+    _abl = lib
+    return lib
+
+
+def moe_ablation_atomic_token_centric(dims, w: DeviceWeights, x, T, topk_idx, topk_gate, out,
+                                      stream=None):
+    _check(load_ablation().moe_ablation_atomic_token_centric(
+        ctypes.byref(dims), ctypes.byref(w.struct), _ptr(x), int(T), _ptr(topk_idx),
+        _ptr(topk_gate), _ptr(out), _stream(stream)), "moe_ablation_atomic_token_centric")
+
+
 # ---------------------------------------------------------------- convenience
 
 class MoELayer:

@@ -1,4 +1,6 @@
-"""Build the gfx950 shared library ``libmoe_mi355x.so`` in-tree with hipcc.
+"""Build the gfx950 shared libraries in-tree with hipcc: the layer library
+``libmoe_mi355x.so`` and the ablation library ``libmoe_ablation.so``
+(token-centric atomic experts, a measurement contrast kept apart).
 
 Usage: python -m mixture_experts_layer_22_amd.build   (or build() from Python)
 """
@@ -14,6 +16,10 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "combine.hip"]
+ABL_DIR = os.path.join(HERE, "ablation")
+ABL_NAME = "libmoe_ablation.so"
+ABL_PATH = os.path.join(HERE, ABL_NAME)
+ABL_SOURCES = ["token_centric.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -39,19 +45,25 @@ def _run(cmd):
 
 
 def build(verbose: bool = False, jobs: int = 5) -> str:
-    """Compile every source for gfx950 and link the shared library.
+    """Compile every source for gfx950 and link the layer library (returns
+    its path), then the ablation library."""
+    path = _build_lib(CSRC, SOURCES, LIB_NAME, LIB_PATH, verbose, jobs)
+    if os.path.isdir(ABL_DIR):
+        _build_lib(ABL_DIR, ABL_SOURCES, ABL_NAME, ABL_PATH, verbose, jobs)
+    return path
 
-    Always recompiles (sources are few; each takes seconds).  Objects are
+
+def _build_lib(src_dir, sources, lib_name, lib_path, verbose, jobs) -> str:
+    """Always recompiles (sources are few; each takes seconds).  Objects are
     compiled in parallel into a temporary directory, then linked into
-    LIB_PATH atomically.
-    """
+    lib_path atomically."""
     with tempfile.TemporaryDirectory(prefix="moe_build_") as tmp:
         procs = []
         objs = []
-        for src in SOURCES:
+        for src in sources:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *FLAGS, "-c", os.path.join(src_dir, src), "-o", obj]
             procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                                 stderr=subprocess.STDOUT, text=True)))
             if len([p for _, p in procs if p.poll() is None]) >= jobs:
@@ -67,11 +79,11 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
             for cmd, out in failed:
                 sys.stderr.write(out)
             raise RuntimeError("hipcc failed: " + "; ".join(" ".join(c[-3:]) for c, _ in failed))
-        tmp_lib = os.path.join(tmp, LIB_NAME)
+        tmp_lib = os.path.join(tmp, lib_name)
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib])
-        os.replace(tmp_lib, LIB_PATH) if os.path.dirname(tmp_lib) == os.path.dirname(LIB_PATH) \
-            else _copy(tmp_lib, LIB_PATH)
-    return LIB_PATH
+        os.replace(tmp_lib, lib_path) if os.path.dirname(tmp_lib) == os.path.dirname(lib_path) \
+            else _copy(tmp_lib, lib_path)
+    return lib_path
 
 
 def _copy(src, dst):

@@ -174,3 +174,46 @@ def test_T_zero_is_noop(lib):
                          None) == B.MOE_OK
     assert lib.moe_combine(ctypes.byref(dims), ctypes.byref(w), None, 0, None, None, None, None,
                            None, None, None) == B.MOE_OK
+
+
+# ---------------------------------------------------------------- ablation library
+
+ABL_HEADER = os.path.join(ROOT, "include", "moe_ablation.h")
+
+
+@pytest.fixture(scope="module")
+def abl():
+    if not os.path.exists(B.ABL_PATH):
+        pytest.fail("libmoe_ablation.so is not built (run __graft_entry__.build())")
+    return B.load_ablation()
+
+
+def test_ablation_exports_every_declared_symbol(abl):
+    src = re.sub(r"/\*.*?\*/", "", open(ABL_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    assert set(names) == set(B.ABL_EXPORTED)
+    for n in names:
+        assert hasattr(abl, n), n
+
+
+def test_ablation_rejects_on_host(abl):
+    f = abl.moe_ablation_atomic_token_centric
+    pk = _dims("atomic-pk")
+    w = _weights()
+    P = FAKE
+    ok_args = (ctypes.byref(w), P, 8, P, P, P, None)
+    # softmax layers and layers with a shared MLP are not the ablation's subject
+    assert f(ctypes.byref(_dims()), *ok_args) == B.MOE_ERR_UNSUPPORTED
+    with_shared = _dims("atomic-pk")
+    with_shared.n_shared, with_shared.f_shared = 1, 64
+    assert f(ctypes.byref(with_shared), *ok_args) == B.MOE_ERR_UNSUPPORTED
+    assert f(None, *ok_args) == B.MOE_ERR_NULL
+    assert f(ctypes.byref(pk), ctypes.byref(w), P, -1, P, P, P, None) == B.MOE_ERR_SHAPE
+    assert f(ctypes.byref(pk), ctypes.byref(w), P, 0, None, None, None, None) == B.MOE_OK
+    assert f(ctypes.byref(pk), ctypes.byref(w), P, 8, None, P, P, None) == B.MOE_ERR_NULL
+    assert f(ctypes.byref(pk), ctypes.byref(_weights(atom_w=None)), P, 8, P, P, P,
+             None) == B.MOE_ERR_NULL
+    assert f(ctypes.byref(pk), ctypes.byref(w), P + 4, 8, P, P, P, None) == B.MOE_ERR_SHAPE
+    bad = _dims("atomic-pk")
+    bad.dtype = 7
+    assert f(ctypes.byref(bad), *ok_args) == B.MOE_ERR_DTYPE
