@@ -123,7 +123,14 @@ typedef struct moe_dims {
  *   shared_gate, shared_up [n_shared, f_shared, d]; shared_down [n_shared, d, f_shared]
  *   const_wc     f32 [n_const, 2, d];  const_v [n_const, d]  (n_const = number
  *                of MOE_ZC_CONST entries, in zc_kind order)
- *   atom_u, atom_w [E, d]  (the atomic experts' in- and out-vectors) */
+ *   atom_u, atom_w [E, d]  (the atomic experts' in- and out-vectors)
+ *   router_residual  f32 [T, E] or NULL: a per-call input, not a parameter.
+ *                The gating residual of the MoE++ page ("Approach": router
+ *                scores carried over from the previous layer): the previous
+ *                layer's logits (as moe_router_logits writes them), added
+ *                to this layer's logits after the bias and before tau.
+ *                Softmax router only (MOE_ERR_UNSUPPORTED with the product
+ *                key); rows are tokens of this call. */
 typedef struct moe_weights {
   const float* router_w;
   const float* router_bias;
@@ -137,6 +144,7 @@ typedef struct moe_weights {
   const void* const_v;
   const void* atom_u;
   const void* atom_w;
+  const float* router_residual;
 } moe_weights;
 
 /* Human-readable name of a status code (static string). */
@@ -153,7 +161,8 @@ int32_t moe_workspace_size(const moe_dims* dims, int64_t T, size_t* bytes);
  *   topk_idx  out: int32 [T, k], expert ids in descending score order, ties
  *             to the lower id.
  *   topk_gate out: f32 [T, k].
- * Softmax router: logit l_e = (x . R_e) + b_e, scaled by tau for e < E_ffn;
+ * Softmax router: logit l_e = (x . R_e) + b_e (+ r_e, the gating residual
+ * w->router_residual[t, e] when given), scaled by tau for e < E_ffn;
  * gates are softmax(l) over all E read at the chosen experts (renormalised
  * over the k when dims->renorm).  Product key: s_r = x[:d/2] . K_r,
  * s_c = x[d/2:] . K_c; top pk_k_row rows x top pk_k_col columns form the
@@ -162,6 +171,15 @@ int32_t moe_workspace_size(const moe_dims* dims, int64_t T, size_t* bytes);
 int32_t moe_route(const moe_dims* dims, const moe_weights* w, const void* x,
                   int64_t T, int32_t* topk_idx, float* topk_gate,
                   void* ws, size_t ws_bytes, moe_stream stream);
+
+/* The softmax router's logits before tau, for a next layer's gating
+ * residual (MoE++ page "Approach"): logits[t, e] = (x . R_e) + b_e (+ the
+ * residual w->router_residual[t, e] when given), f32 [T, E], the same
+ * values moe_route selects on before scaling the FFN experts' by tau.
+ * Product key: MOE_ERR_UNSUPPORTED.  Workspace as for moe_route. */
+int32_t moe_router_logits(const moe_dims* dims, const moe_weights* w, const void* x,
+                          int64_t T, float* logits, void* ws, size_t ws_bytes,
+                          moe_stream stream);
 
 /* Expert-centric dispatch (OmniMoE page sec. 2.2, Task Collection and
  * Grouping & Sorting): a stable sort of the T*k tasks by expert id.

@@ -26,8 +26,9 @@ MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 4, 5, 6
 MOE_F32, MOE_BF16 = 0, 1
 MOE_MAX_ZC = 8
 
-EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route", "moe_dispatch",
-            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_traced"]
+EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route", "moe_router_logits",
+            "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+            "moe_forward_traced"]
 MOE_N_PHASES = 6
 PHASES = ["route", "dispatch", "tiles", "expert1", "expert2", "combine"]
 
@@ -50,8 +51,11 @@ class MoeDims(ctypes.Structure):
                 ("zc_kind", ctypes.c_int32 * MOE_MAX_ZC)]
 
 
+# router_residual is a per-call input (the gating residual), carried in the
+# same struct as the C ABI does
 _WEIGHT_FIELDS = ["router_w", "router_bias", "w_gate", "w_up", "w_down", "shared_gate",
-                  "shared_up", "shared_down", "const_wc", "const_v", "atom_u", "atom_w"]
+                  "shared_up", "shared_down", "const_wc", "const_v", "atom_u", "atom_w",
+                  "router_residual"]
 
 
 class MoeWeights(ctypes.Structure):
@@ -79,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_workspace_size.argtypes = [dims_p, i64, ctypes.POINTER(sz)]
     lib.moe_route.restype = ctypes.c_int32
     lib.moe_route.argtypes = [dims_p, w_p, P, i64, P, P, P, sz, P]
+    lib.moe_router_logits.restype = ctypes.c_int32
+    lib.moe_router_logits.argtypes = [dims_p, w_p, P, i64, P, P, sz, P]
     lib.moe_dispatch.restype = ctypes.c_int32
     lib.moe_dispatch.argtypes = [dims_p, P, i64, P, P, P, P, P, sz, P]
     lib.moe_expert_ffn.restype = ctypes.c_int32
@@ -151,6 +157,16 @@ class DeviceWeights:
         for n in _WEIGHT_FIELDS:
             setattr(self.struct, n, _ptr(self.tensors.get(n)))
 
+    def set_residual(self, residual: Optional[torch.Tensor]):
+        """Gating residual for the following calls: f32 [T, E] on the device
+        (kept referenced here), or None."""
+        if residual is None:
+            self.tensors.pop("router_residual", None)
+        else:
+            assert residual.dtype == torch.float32 and residual.is_contiguous()
+            self.tensors["router_residual"] = residual
+        self.struct.router_residual = _ptr(self.tensors.get("router_residual"))
+
 
 # ---------------------------------------------------------------- entry points
 
@@ -169,6 +185,12 @@ def moe_route(dims, w: DeviceWeights, x, T, topk_idx, topk_gate, ws, stream=None
     _check(load().moe_route(ctypes.byref(dims), ctypes.byref(w.struct), _ptr(x), int(T),
                             _ptr(topk_idx), _ptr(topk_gate), _ptr(ws),
                             0 if ws is None else ws.numel(), _stream(stream)), "moe_route")
+
+
+def moe_router_logits(dims, w: DeviceWeights, x, T, logits, ws, stream=None):
+    _check(load().moe_router_logits(ctypes.byref(dims), ctypes.byref(w.struct), _ptr(x), int(T),
+                                    _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(stream)), "moe_router_logits")
 
 
 def moe_dispatch(dims, topk_idx, T, counts, offsets, perm, inv_perm, ws, stream=None):

@@ -134,9 +134,10 @@ int32_t check_weights(const moe_dims* d, const moe_weights* w, bool router, bool
   if (experts && is_pk(d) && !w->atom_u) return MOE_ERR_NULL;
   if (combine && is_pk(d) && !w->atom_w) return MOE_ERR_NULL;
   if (combine && n_const_of(d) > 0 && (!w->const_wc || !w->const_v)) return MOE_ERR_NULL;
+  if (router && is_pk(d) && w->router_residual) return MOE_ERR_UNSUPPORTED;
   const void* ps[] = {w->router_w, w->router_bias, w->w_gate, w->w_up, w->w_down,
                       w->shared_gate, w->shared_up, w->shared_down, w->const_wc, w->const_v,
-                      w->atom_u, w->atom_w};
+                      w->atom_u, w->atom_w, w->router_residual};
   for (const void* p : ps)
     if (misaligned(p)) return MOE_ERR_SHAPE;
   return MOE_OK;
@@ -152,7 +153,7 @@ int32_t do_route(const moe_dims* d, const moe_weights* w, const void* x, int64_t
     MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, d->E, d->d, logits, d->E, 0,
                                  L.splits, st));
     MOE_TRY(launch_select_topk(logits, L.splits, T, d->E, d->E_ffn, d->k, d->ffn_logit_scale,
-                               w->router_bias, d->renorm, idx, gate, st));
+                               w->router_bias, w->router_residual, d->renorm, idx, gate, st));
   } else {
     const int K = L.Kw;
     const float* Wc = W + (size_t)d->pk_rows * K;
@@ -325,6 +326,26 @@ int32_t moe_route(const moe_dims* dims, const moe_weights* w, const void* x, int
   if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   return do_route(dims, w, x, T, topk_idx, topk_gate, ws, L, (hipStream_t)stream);
+}
+
+int32_t moe_router_logits(const moe_dims* dims, const moe_weights* w, const void* x, int64_t T,
+                          float* logits, void* ws, size_t ws_bytes, moe_stream stream) {
+  int32_t s = validate_dims(dims, T);
+  if (s != MOE_OK) return s;
+  if (is_pk(dims)) return MOE_ERR_UNSUPPORTED;
+  if ((s = check_weights(dims, w, true, false, false)) != MOE_OK) return s;
+  if (T > 0 && (!x || !logits)) return MOE_ERR_NULL;
+  if (misaligned(x) || misaligned(logits)) return MOE_ERR_SHAPE;
+  Layout L = make_layout(dims, T);
+  if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  const hipStream_t st = (hipStream_t)stream;
+  float* part = at<float*>(ws, L.logits);
+  MOE_TRY(launch_router_logits(dims->dtype, x, T, dims->d, 0, w->router_w, dims->E, dims->d,
+                               part, dims->E, 0, L.splits, st));
+  MOE_TRY(launch_logits_out(part, L.splits, T, dims->E, w->router_bias, w->router_residual,
+                            logits, st));
+  return MOE_OK;
 }
 
 int32_t moe_dispatch(const moe_dims* dims, const int32_t* topk_idx, int64_t T, int32_t* counts,

@@ -60,8 +60,12 @@ hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, in
                                 const float* W, int NL, int K, float* logits,
                                 int ldl, int col_off, int splits, hipStream_t st);
 hipError_t launch_select_topk(const float* logits, int splits, int64_t T, int E, int E_ffn, int k,
-                              float tau, const float* bias, int renorm, int32_t* idx, float* gate,
-                              hipStream_t st);
+                              float tau, const float* bias, const float* residual, int renorm,
+                              int32_t* idx, float* gate, hipStream_t st);
+// Softmax router logits before tau: sum of the K-split partials + bias (+
+// gating residual), f32 [T, E]
+hipError_t launch_logits_out(const float* part, int splits, int64_t T, int E, const float* bias,
+                             const float* residual, float* out, hipStream_t st);
 hipError_t launch_select_pk(const float* scores, int splits, int64_t T, int rows, int cols,
                             int krow, int kcol, int k, int32_t* idx, float* gate, hipStream_t st);
 

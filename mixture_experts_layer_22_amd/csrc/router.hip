@@ -159,14 +159,17 @@ __global__ void k_router_logits_f32(const float* __restrict__ x, int64_t T, int 
 
 // ------------------------------------------------------------------------
 // Softmax top-k selection, one wave per token.  V = values per lane
-// (E <= 64 V).  Logit l = fl32(dot + bias), then fl32(tau * l) for FFN
-// experts.  Order (-l, e); gates = softmax over all E at the chosen ones,
-// optionally renormalised over the k.
+// (E <= 64 V).  Logit l = fl32(dot + bias), plus the gating residual r of
+// the MoE++ page ("Approach": router scores carried over from the previous
+// layer) when given, then fl32(tau * l) for FFN experts.  Order (-l, e);
+// gates = softmax over all E at the chosen ones, optionally renormalised
+// over the k.
 template <int V>
 __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ logits, int nparts,
                                                     int64_t part_stride, int64_t T,
                                                     int E, int E_ffn, int k, float tau,
-                                                    const float* __restrict__ bias, int renorm,
+                                                    const float* __restrict__ bias,
+                                                    const float* __restrict__ residual, int renorm,
                                                     int32_t* __restrict__ idx_out,
                                                     float* __restrict__ gate_out) {
   const int lane = threadIdx.x & 63;
@@ -182,6 +185,7 @@ __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ l
       l = row[e];
       for (int z = 1; z < nparts; z++) l += row[z * part_stride + e];
       if (bias) l = l + bias[e];
+      if (residual) l = l + residual[t * E + e];
       if (e < E_ffn) l = tau * l;
     }
     v[i] = l;
@@ -435,17 +439,43 @@ hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, in
 }
 
 hipError_t launch_select_topk(const float* logits, int splits, int64_t T, int E, int E_ffn, int k,
-                              float tau, const float* bias, int renorm, int32_t* idx, float* gate,
-                              hipStream_t st) {
+                              float tau, const float* bias, const float* residual, int renorm,
+                              int32_t* idx, float* gate, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv(T, 4)), block(256);
   int V = (int)cdiv(E, 64);
 #define SEL(VV) hipLaunchKernelGGL(k_select_topk<VV>, grid, block, 0, st, logits, splits, \
-                                   (int64_t)T * E, T, E, E_ffn, k, tau, bias, renorm, idx, gate)
+                                   (int64_t)T * E, T, E, E_ffn, k, tau, bias, residual, renorm, \
+                                   idx, gate)
   if (V <= 1) SEL(1);
   else if (V <= 2) SEL(2);
   else SEL(4);
 #undef SEL
+  return hipGetLastError();
+}
+
+// Router logits before tau (for a next layer's gating residual): the same
+// fl32 sums k_select_topk forms, in the same order, written out.
+__global__ __launch_bounds__(256) void k_logits_out(const float* __restrict__ part, int nparts,
+                                                   int64_t part_stride, int64_t n, int E,
+                                                   const float* __restrict__ bias,
+                                                   const float* __restrict__ residual,
+                                                   float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float l = part[i];
+  for (int z = 1; z < nparts; z++) l += part[z * part_stride + i];
+  if (bias) l = l + bias[i % E];
+  if (residual) l = l + residual[i];
+  out[i] = l;
+}
+
+hipError_t launch_logits_out(const float* part, int splits, int64_t T, int E, const float* bias,
+                             const float* residual, float* out, hipStream_t st) {
+  const int64_t n = T * E;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_logits_out, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, part, splits,
+                     n, n, E, bias, residual, out);
   return hipGetLastError();
 }
 

@@ -101,6 +101,13 @@ CONFIGS: Dict[str, LayerConfig] = _base_configs()
 CONFIG_ORDER = ["tiny-fp32", "deepseek16b", "qwen3-decode", "moepp", "atomic-pk"]
 
 
+def make_residual(cfg: LayerConfig, seed: int, scale: float = 1.0) -> np.ndarray:
+    """A stand-in for a previous layer's router logits (the gating residual's
+    input): float32 [T, E], N(0, scale^2), from its own seeded stream."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.standard_normal((cfg.T, cfg.E), dtype=np.float32) * np.float32(scale))
+
+
 def small_variant(name: str, seed: int = 7) -> LayerConfig:
     """A shrunken version of a workload with the same structure.
 

@@ -83,32 +83,44 @@ def order_desc(scores: np.ndarray) -> np.ndarray:
     return np.argsort(-scores, axis=-1, kind="stable")
 
 
-def router_logits(cfg, x, router_w, router_bias=None) -> np.ndarray:
+def router_logits(cfg, x, router_w, router_bias=None, residual=None) -> np.ndarray:
     """Router logits l'[T, E] (float32).
 
     [OMNI] sec. 1 names the per-token O(N d) router projection as the standard
     scheme; [MOEPP] "Approach" routes over FFN and zero-computation experts
     together, and its tau scales the FFN experts (smaller tau sends more
     tokens to zero-computation experts).  Reading: tau multiplies the FFN
-    logits only.
+    logits only.  [MOEPP] "Approach" also carries router scores over from the
+    previous layer (gating residuals); reading: the previous layer's logits
+    before its tau (`residual` [T, E] float32) are added after the bias, in
+    float32, before this layer's tau.
     """
-    l = dot_f32(as_f64(x), as_f64(router_w))
-    if router_bias is not None:
-        l = l + np.asarray(router_bias, dtype=np.float32)
+    l = pre_tau_logits(x, router_w, router_bias, residual)
     if cfg.E_ffn < cfg.E or cfg.tau != 1.0:
         l = l.copy()
         l[:, :cfg.E_ffn] = np.float32(cfg.tau) * l[:, :cfg.E_ffn]
     return l.astype(np.float32)
 
 
-def route_softmax_topk(cfg, x, router_w, router_bias=None):
+def pre_tau_logits(x, router_w, router_bias=None, residual=None) -> np.ndarray:
+    """fl32(x . R_e) + b_e (+ r_e): the logits a next layer takes as its
+    gating residual (float32 [T, E])."""
+    l = dot_f32(as_f64(x), as_f64(router_w))
+    if router_bias is not None:
+        l = l + np.asarray(router_bias, dtype=np.float32)
+    if residual is not None:
+        l = l + np.asarray(residual, dtype=np.float32)
+    return l.astype(np.float32)
+
+
+def route_softmax_topk(cfg, x, router_w, router_bias=None, residual=None):
     """Top-k softmax gating.  Returns (idx int32 [T,k], gate f64 [T,k], logits f32).
 
     Selection: the first k experts in (-l', e) order.  Gates: softmax of l'
     over all E experts read at the chosen ones, renormalised over the k
     chosen when cfg.renorm.
     """
-    l = router_logits(cfg, x, router_w, router_bias)
+    l = router_logits(cfg, x, router_w, router_bias, residual)
     idx = order_desc(l)[:, :cfg.k].astype(np.int32)
     p = softmax(l.astype(np.float64), axis=1)
     gate = np.take_along_axis(p, idx, axis=1)
@@ -155,7 +167,7 @@ def route(cfg, inp):
     if cfg.router == 1:
         return route_product_key(cfg, inp["x"], inp["router_w"])
     idx, gate, l = route_softmax_topk(cfg, inp["x"], inp["router_w"],
-                                      inp.get("router_bias"))
+                                      inp.get("router_bias"), inp.get("router_residual"))
     return idx, gate, {"logits": l}
 
 

@@ -36,7 +36,8 @@ def max_rel_l2(got, ref):
 def check_softmax_routing(cfg, inp, idx_gpu, gate_gpu):
     """Returns the number of tokens accepted only through the near-tie rule."""
     idx_ref, gate_ref, l = O.route_softmax_topk(cfg, inp["x"], inp["router_w"],
-                                                inp.get("router_bias"))
+                                                inp.get("router_bias"),
+                                                inp.get("router_residual"))
     idx_gpu = np.asarray(idx_gpu)
     ties = 0
     for t in np.nonzero(np.any(idx_gpu != idx_ref, axis=1))[0]:

@@ -217,3 +217,25 @@ def test_ablation_rejects_on_host(abl):
     bad = _dims("atomic-pk")
     bad.dtype = 7
     assert f(ctypes.byref(bad), *ok_args) == B.MOE_ERR_DTYPE
+
+
+def test_router_logits_and_residual_rejections(lib):
+    dims = _dims()
+    _, need = _ws_size(dims, 8)
+    w = _weights(router_residual=None)
+    P = FAKE
+    f = lib.moe_router_logits
+    assert f(ctypes.byref(dims), ctypes.byref(w), P, 8, None, P, need, None) == B.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), ctypes.byref(w), P, 8, P, P, need - 1,
+             None) == B.MOE_ERR_WORKSPACE
+    assert f(ctypes.byref(dims), ctypes.byref(w), P, 8, P + 4, P, need, None) == B.MOE_ERR_SHAPE
+    assert f(ctypes.byref(dims), ctypes.byref(w), P, 0, None, P, need, None) == B.MOE_OK
+    pk = _dims("atomic-pk")
+    _, need_pk = _ws_size(pk, 8)
+    assert f(ctypes.byref(pk), ctypes.byref(w), P, 8, P, P, need_pk, None) == B.MOE_ERR_UNSUPPORTED
+    # a gating residual with the product-key router
+    assert lib.moe_route(ctypes.byref(pk), ctypes.byref(_weights(router_residual=P)), P, 8, P, P,
+                         P, need_pk, None) == B.MOE_ERR_UNSUPPORTED
+    # misaligned residual
+    assert lib.moe_route(ctypes.byref(dims), ctypes.byref(_weights(router_residual=P + 4)), P, 8,
+                         P, P, P, need, None) == B.MOE_ERR_SHAPE

@@ -229,3 +229,61 @@ def test_deterministic(name):
     b = layer.forward(x).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ gating residual
+
+@pytest.mark.parametrize("name", ["deepseek16b", "moepp", "tiny-fp32"])
+def test_gating_residual(name):
+    """MoE++ gating residual: a [T, E] previous-layer score input added to
+    the logits; routing and outputs against the oracle with the same input."""
+    cfg = I.small_variant(name) if name != "tiny-fp32" else I.CONFIGS[name]
+    inp = dict(I.make_inputs(cfg))
+    inp["router_residual"] = I.make_residual(cfg, seed=77, scale=2.0)
+    say("gating residual", name)
+    layer = make_layer(cfg, inp)
+    assert layer.weights.struct.router_residual   # uploaded with the inputs
+    x = x_dev(inp)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
+    out = layer.forward(x, topk_idx=idx, topk_gate=gate)
+    torch.cuda.synchronize()
+    idx_np, gate_np = idx.cpu().numpy(), gate.cpu().numpy()
+    C.check_routing(cfg, inp, idx_np, gate_np)
+    # the residual really moved the routing
+    plain = {k: v for k, v in inp.items() if k != "router_residual"}
+    idx0, _, _ = O.route(cfg, plain)
+    assert np.mean(np.any(idx0 != idx_np, axis=1)) > 0.2
+    ref, _, _ = O.forward(cfg, inp, idx_np, gate_np.astype(np.float64))
+    assert C.max_rel_l2(np_of(out), ref) <= C.out_tol(cfg)
+
+
+def test_router_logits_and_chained_residual():
+    """moe_router_logits against the oracle's pre-tau logits, then fed to a
+    second layer of the same shape as its gating residual."""
+    cfg1 = I.small_variant("moepp")
+    cfg2 = cfg1.replace(seed=cfg1.seed + 1)
+    inp1, inp2 = I.make_inputs(cfg1), dict(I.make_inputs(cfg2))
+    inp1 = dict(inp1)
+    inp1["router_residual"] = I.make_residual(cfg1, seed=78)
+    l1 = make_layer(cfg1, inp1)
+    x = x_dev(inp1)
+    logits = torch.empty((cfg1.T, cfg1.E), dtype=torch.float32, device=DEV)
+    B.moe_router_logits(l1.dims, l1.weights, x, cfg1.T, logits, l1.workspace(cfg1.T))
+    torch.cuda.synchronize()
+    ref = O.pre_tau_logits(inp1["x"], inp1["router_w"], inp1.get("router_bias"),
+                           inp1["router_residual"])
+    got = logits.cpu().numpy()
+    # fp32 accumulation order differs from the oracle's single rounding
+    assert np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))) <= 2e-5
+    inp2["x"] = inp1["x"]
+    inp2["router_residual"] = got
+    l2 = make_layer(cfg2, inp2)
+    idx = torch.empty((cfg2.T, cfg2.k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((cfg2.T, cfg2.k), dtype=torch.float32, device=DEV)
+    out = l2.forward(x, topk_idx=idx, topk_gate=gate)
+    torch.cuda.synchronize()
+    idx_np, gate_np = idx.cpu().numpy(), gate.cpu().numpy()
+    C.check_routing(cfg2, inp2, idx_np, gate_np)
+    r2, _, _ = O.forward(cfg2, inp2, idx_np, gate_np.astype(np.float64))
+    assert C.max_rel_l2(np_of(out), r2) <= C.out_tol(cfg2)

@@ -32,15 +32,25 @@ def _run_pins():
     return failed
 
 
-def _no_bias(cfg, x, router_w, router_bias=None, _orig=O.router_logits):
-    return _orig(cfg, x, router_w, None)
+def _no_bias(cfg, x, router_w, router_bias=None, residual=None, _orig=O.router_logits):
+    return _orig(cfg, x, router_w, None, residual)
 
 
-def _tau_everywhere(cfg, x, router_w, router_bias=None):
-    l = O.dot_f32(O.as_f64(x), O.as_f64(router_w))
-    if router_bias is not None:
-        l = l + np.asarray(router_bias, np.float32)
+def _tau_everywhere(cfg, x, router_w, router_bias=None, residual=None):
+    l = O.pre_tau_logits(x, router_w, router_bias, residual)
     return (np.float32(cfg.tau) * l).astype(np.float32)
+
+
+def _residual_dropped(x, router_w, router_bias=None, residual=None, _orig=O.pre_tau_logits):
+    return _orig(x, router_w, router_bias, None)
+
+
+def _residual_after_tau(cfg, x, router_w, router_bias=None, residual=None,
+                        _orig=O.router_logits):
+    l = _orig(cfg, x, router_w, router_bias, None)
+    if residual is not None:
+        l = (l + np.asarray(residual, np.float32)).astype(np.float32)
+    return l
 
 
 def _ties_high(scores):
@@ -77,8 +87,8 @@ def _pk_rows_cols_swapped(cfg, x, router_w, _orig=O.route_product_key):
     return _orig(cfg, xs, router_w)
 
 
-def _no_renorm(cfg, x, router_w, router_bias=None, _orig=O.route_softmax_topk):
-    return _orig(cfg.replace(renorm=False), x, router_w, router_bias)
+def _no_renorm(cfg, x, router_w, router_bias=None, residual=None, _orig=O.route_softmax_topk):
+    return _orig(cfg.replace(renorm=False), x, router_w, router_bias, residual)
 
 
 def _softmax_no_shift_wrong_axis(z, axis=-1):
@@ -94,6 +104,8 @@ def _combine_no_shared(cfg, inp, idx, gate, inv_perm, Y, SY, tokens=None, _orig=
 MUTANTS = {
     "router_logits": _no_bias,
     "router_logits#tau": _tau_everywhere,
+    "router_logits#residual_after_tau": _residual_after_tau,
+    "pre_tau_logits#residual_dropped": _residual_dropped,
     "order_desc": _ties_high,
     "swiglu": _swiglu_swapped,
     "silu": _silu_sign,

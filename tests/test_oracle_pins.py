@@ -83,6 +83,70 @@ def test_router_logits_onehot_bias_tau():
         assert np.array_equal(l[:, e], want.astype(np.float32))
 
 
+def test_gating_residual_placement():
+    """MoE++ "Approach" gating residual (reading: the previous layer's logits,
+    added after the bias and before tau).  With one-hot router rows and
+    small dyadic values every step is exact, so l = tau * (x + b + r) on the
+    FFN experts and x + b + r on the zero-computation ones, by hand."""
+    cfg = _softmax_cfg(E=5, E_ffn=3, tau=0.5, zc_kinds=[I.ZC_ZERO, I.ZC_COPY])
+    rng = np.random.default_rng(11)
+    x = (rng.integers(-8, 8, size=(cfg.T, cfg.d)) / 4).astype(np.float32)
+    pick = [3, 0, 7, 2, 5]
+    R = np.zeros((cfg.E, cfg.d), np.float32)
+    R[np.arange(cfg.E), pick] = 1.0
+    b = np.array([0.25, -1.0, 0.5, 2.0, -0.125], np.float32)
+    r = (rng.integers(-16, 16, size=(cfg.T, cfg.E)) / 8).astype(np.float32)
+    l = O.router_logits(cfg, x, R, b, r)
+    for e in range(cfg.E):
+        want = x[:, pick[e]] + b[e] + r[:, e]
+        if e < cfg.E_ffn:
+            want = 0.5 * want
+        assert np.array_equal(l[:, e], want.astype(np.float32))
+    # the logits a next layer takes are the same sums before tau
+    pre = O.pre_tau_logits(x, R, b, r)
+    assert np.array_equal(pre, (x[:, pick] + b[None, :] + r).astype(np.float32))
+
+
+def test_gating_residual_zero_and_steering():
+    """A zero residual changes nothing; a residual far above every logit on
+    one expert makes it every token's first choice (softmax top-k by hand)."""
+    cfg = _softmax_cfg(T=30, d=16, E=7, E_ffn=7, k=2)
+    rng = np.random.default_rng(12)
+    x = rng.normal(size=(cfg.T, cfg.d)).astype(np.float32)
+    R = rng.normal(size=(cfg.E, cfg.d)).astype(np.float32)
+    i0, g0, l0 = O.route_softmax_topk(cfg, x, R)
+    i1, g1, l1 = O.route_softmax_topk(cfg, x, R, None, np.zeros((cfg.T, cfg.E), np.float32))
+    assert np.array_equal(i0, i1) and np.array_equal(l0, l1) and np.allclose(g0, g1)
+    r = np.zeros((cfg.T, cfg.E), np.float32)
+    r[:, 5] = 1e4
+    i2, g2, _ = O.route_softmax_topk(cfg, x, R, None, r)
+    assert np.all(i2[:, 0] == 5)
+    # the second choice is the best of the others, as without the residual
+    for t in range(cfg.T):
+        rest = sorted((e for e in range(cfg.E) if e != 5), key=lambda e: (-l0[t, e], e))
+        assert i2[t, 1] == rest[0]
+    assert np.all(g2[:, 0] > 0.999)
+
+
+def test_gating_residual_chained_layers():
+    """Layer 2 with layer 1's pre-tau logits as residual: every logit is the
+    float32 sum of two single-rounded dot products and two biases, checked
+    term by term with math.fsum."""
+    cfg = _softmax_cfg(T=5, d=32, E=4, E_ffn=4)
+    rng = np.random.default_rng(13)
+    x = rng.normal(size=(cfg.T, cfg.d)).astype(np.float32)
+    R1, R2 = (rng.normal(size=(2, cfg.E, cfg.d)) / 4).astype(np.float32)
+    b1, b2 = rng.normal(size=(2, cfg.E)).astype(np.float32)
+    l1 = O.pre_tau_logits(x, R1, b1)
+    l2 = O.router_logits(cfg, x, R2, b2, l1)
+    for t in range(cfg.T):
+        for e in range(cfg.E):
+            d1 = np.float32(exact_dot_f32(x[t], R1[e]))
+            d2 = np.float32(exact_dot_f32(x[t], R2[e]))
+            want = np.float32(np.float32(d2 + b2[e]) + np.float32(d1 + b1[e]))
+            assert l2[t, e] == want
+
+
 def test_router_logits_brute_force_exact_rounding():
     cfg = _softmax_cfg(T=6, d=64, E=5, E_ffn=5)
     rng = np.random.default_rng(2)
