@@ -149,18 +149,20 @@ int32_t do_route(const moe_dims* d, const moe_weights* w, const void* x, int64_t
                  float* gate, void* ws, const Layout& L, hipStream_t st) {
   float* logits = at<float*>(ws, L.logits);
   const float* W = w->router_w;
+  const RouterPart none = {nullptr, 0, 0, 0, 0};
   if (!is_pk(d)) {
-    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, d->E, d->d, logits, d->E, 0,
-                                 L.splits, st));
+    const RouterPart all = {W, d->E, 0, 0, 0};
+    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, all, none, d->d, logits, d->E, L.splits,
+                                 st));
     MOE_TRY(launch_select_topk(logits, L.splits, T, d->E, d->E_ffn, d->k, d->ffn_logit_scale,
                                w->router_bias, w->router_residual, d->renorm, idx, gate, st));
   } else {
     const int K = L.Kw;
     const float* Wc = W + (size_t)d->pk_rows * K;
-    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, 0, W, d->pk_rows, K, logits, L.NL,
-                                 0, L.splits, st));
-    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, K, Wc, d->pk_cols, K, logits, L.NL,
-                                 d->pk_rows, L.splits, st));
+    const RouterPart rows = {W, d->pk_rows, 0, 0, 0};
+    const RouterPart cols = {Wc, d->pk_cols, K, d->pk_rows, 0};
+    MOE_TRY(launch_router_logits(d->dtype, x, T, d->d, rows, cols, K, logits, L.NL, L.splits,
+                                 st));
     MOE_TRY(launch_select_pk(logits, L.splits, T, d->pk_rows, d->pk_cols, d->pk_k_row,
                              d->pk_k_col, d->k, idx, gate, st));
   }
@@ -341,8 +343,10 @@ int32_t moe_router_logits(const moe_dims* dims, const moe_weights* w, const void
   if (T == 0) return MOE_OK;
   const hipStream_t st = (hipStream_t)stream;
   float* part = at<float*>(ws, L.logits);
-  MOE_TRY(launch_router_logits(dims->dtype, x, T, dims->d, 0, w->router_w, dims->E, dims->d,
-                               part, dims->E, 0, L.splits, st));
+  const RouterPart all = {w->router_w, dims->E, 0, 0, 0};
+  const RouterPart none = {nullptr, 0, 0, 0, 0};
+  MOE_TRY(launch_router_logits(dims->dtype, x, T, dims->d, all, none, dims->d, part, dims->E,
+                               L.splits, st));
   MOE_TRY(launch_logits_out(part, L.splits, T, dims->E, w->router_bias, w->router_residual,
                             logits, st));
   return MOE_OK;

@@ -56,9 +56,16 @@ struct CombineArgs {
 
 // router.hip
 int router_splits(int dtype, int64_t T, int NL, int K);
-hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, int x_off,
-                                const float* W, int NL, int K, float* logits,
-                                int ldl, int col_off, int splits, hipStream_t st);
+// One weight block of the router: logits[:, col_off + n] = x[:, x_off + K] .
+// W[n]  (n < NL); ny is set by the launcher.  Up to two parts per launch
+// (the product key's row and column keys); NL = 0 for an unused part.
+struct RouterPart {
+  const float* W;
+  int NL, x_off, col_off, ny;
+};
+hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, RouterPart p0,
+                                RouterPart p1, int K, float* logits, int ldl, int splits,
+                                hipStream_t st);
 hipError_t launch_select_topk(const float* logits, int splits, int64_t T, int E, int E_ffn, int k,
                               float tau, const float* bias, const float* residual, int renorm,
                               int32_t* idx, float* gate, hipStream_t st);

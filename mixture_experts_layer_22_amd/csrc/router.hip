@@ -48,14 +48,19 @@ __device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uin
 __device__ __forceinline__ int rl_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __global__ __launch_bounds__(256) void k_router_logits_bf16(
-    const uint16_t* __restrict__ x, int64_t T, int ldx, int x_off,
-    const float* __restrict__ W, int NL, int K,
-    float* __restrict__ logits, int ldl, int col_off, int64_t part_stride) {
+    const uint16_t* __restrict__ x, int64_t T, int ldx, RouterPart p0, RouterPart p1, int K,
+    float* __restrict__ logits, int ldl, int64_t part_stride) {
   // [buf][slice * 64 + logit][64 K] bf16, 16-byte chunks swizzled
   __shared__ __attribute__((aligned(16))) uint16_t bs[2][3 * 64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = (int64_t)blockIdx.x * 64 + wave * 16;
-  const int n0 = blockIdx.y * 64;
+  // blockIdx.y: the first part's logit blocks, then the second's
+  const bool second = (int)blockIdx.y >= p0.ny;
+  const float* __restrict__ W = second ? p1.W : p0.W;
+  const int NL = second ? p1.NL : p0.NL;
+  const int x_off = second ? p1.x_off : p0.x_off;
+  const int col_off = second ? p1.col_off : p0.col_off;
+  const int n0 = ((int)blockIdx.y - (second ? p0.ny : 0)) * 64;
   const int kc = K / gridDim.z;
   const int kbeg = blockIdx.z * kc, nch = kc / 64;
   const int r = lane & 15, q = lane >> 4;
@@ -100,14 +105,20 @@ __global__ __launch_bounds__(256) void k_router_logits_bf16(
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // x fragments of chunk c + 1 are loaded while chunk c multiplies
+  u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
+  u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 8);
   bload(0);
   bstore(0);
   __syncthreads();
   for (int c = 0; c < nch; c++) {
     const int buf = c & 1;
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap + c * 64);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + c * 64 + 8);
-    if (c + 1 < nch) bload(c + 1);
+    u32x4 an0 = a0, an1 = a1;
+    if (c + 1 < nch) {
+      an0 = *reinterpret_cast<const u32x4*>(ap + (c + 1) * 64);
+      an1 = *reinterpret_cast<const u32x4*>(ap + (c + 1) * 64 + 8);
+      bload(c + 1);
+    }
 #pragma unroll
     for (int p = 0; p < 3; p++)
 #pragma unroll
@@ -122,6 +133,8 @@ __global__ __launch_bounds__(256) void k_router_logits_bf16(
                                                          __builtin_bit_cast(bf16x8, b1), acc[j], 0, 0, 0);
       }
     if (c + 1 < nch) bstore(buf ^ 1);
+    a0 = an0;
+    a1 = an1;
     __syncthreads();
   }
   // lane holds C[4 q + e][16 j + r] of its wave's 16 tokens
@@ -423,17 +436,23 @@ int router_splits(int dtype, int64_t T, int NL, int K) {
   return S;
 }
 
-hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, int x_off,
-                                const float* W, int NL, int K, float* logits,
-                                int ldl, int col_off, int splits, hipStream_t st) {
-  if (T == 0 || NL == 0) return hipSuccess;
+hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, RouterPart p0,
+                                RouterPart p1, int K, float* logits, int ldl, int splits,
+                                hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  p0.ny = (int)cdiv(p0.NL, 64);
+  p1.ny = (int)cdiv(p1.NL, 64);
+  if (p0.ny + p1.ny == 0) return hipSuccess;
   if (dtype == MOE_BF16) {
-    dim3 grid((unsigned)cdiv(T, 64), (unsigned)cdiv(NL, 64), (unsigned)splits);
+    dim3 grid((unsigned)cdiv(T, 64), (unsigned)(p0.ny + p1.ny), (unsigned)splits);
     hipLaunchKernelGGL(k_router_logits_bf16, grid, dim3(256), 0, st, (const uint16_t*)x, T, ldx,
-                       x_off, W, NL, K, logits, ldl, col_off, (int64_t)T * ldl);
+                       p0, p1, K, logits, ldl, (int64_t)T * ldl);
   } else {
-    hipLaunchKernelGGL(k_router_logits_f32, dim3((unsigned)cdiv(T * NL, 256)), dim3(256), 0, st,
-                       (const float*)x, T, ldx, x_off, W, NL, K, logits, ldl, col_off);
+    for (const RouterPart& p : {p0, p1})
+      if (p.NL > 0)
+        hipLaunchKernelGGL(k_router_logits_f32, dim3((unsigned)cdiv(T * p.NL, 256)), dim3(256),
+                           0, st, (const float*)x, T, ldx, p.x_off, p.W, p.NL, K, logits, ldl,
+                           p.col_off);
   }
   return hipGetLastError();
 }
