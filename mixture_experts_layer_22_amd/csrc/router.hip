@@ -36,24 +36,29 @@ __device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uin
 // blocks busy at small T; the selection kernel adds the partials in order z).
 // bf16 x; fp32 W [NL, K].
 //
-// Block: 64 tokens x 64 logits; wave w owns tokens 16w..16w+15 and all 64
-// logits (four v_mfma_f32_16x16x32_bf16 tiles).  Per 64-wide K chunk the
+// Block: MT tokens (64 or 256) x 64 logits; wave w owns tokens
+// w*MT/4 .. +MT/4 (MT/64 blocks of 16) and all 64 logits (four
+// v_mfma_f32_16x16x32_bf16 tiles per token block).  Per 64-wide K chunk the
 // block's 64 fp32 weight rows are read once, split into their three bf16
 // slices and staged in LDS (24 KB, double buffered), shared by the four
-// waves; x fragments go straight from global memory to registers.  K is
-// permuted identically for both operands: lane (r = l%16, q = l/16) takes
-// elements [16q, 16q+16) of the chunk, MFMA step h the half [16q + 8h, +8),
-// so each x row is one 128-byte run.  The three slices accumulate into one
-// fp32 accumulator.
+// waves; x fragments go straight from global memory to registers, one chunk
+// ahead.  The larger block re-splits the weights for 4x the tokens (the
+// product-key layer, with many tokens and no split K).  K is permuted
+// identically for both operands: lane (r = l%16, q = l/16) takes elements
+// [16q, 16q+16) of the chunk, MFMA step h the half [16q + 8h, +8), so each x
+// row is one 128-byte run.  The three slices accumulate into one fp32
+// accumulator.
 __device__ __forceinline__ int rl_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+template <int MT>
 __global__ __launch_bounds__(256) void k_router_logits_bf16(
     const uint16_t* __restrict__ x, int64_t T, int ldx, RouterPart p0, RouterPart p1, int K,
     float* __restrict__ logits, int ldl, int64_t part_stride) {
+  constexpr int MB = MT / 64;  // token blocks of 16 per wave
   // [buf][slice * 64 + logit][64 K] bf16, 16-byte chunks swizzled
   __shared__ __attribute__((aligned(16))) uint16_t bs[2][3 * 64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  const int64_t m0 = (int64_t)blockIdx.x * MT + wave * (MT / 4);
   // blockIdx.y: the first part's logit blocks, then the second's
   const bool second = (int)blockIdx.y >= p0.ny;
   const float* __restrict__ W = second ? p1.W : p0.W;
@@ -64,9 +69,13 @@ __global__ __launch_bounds__(256) void k_router_logits_bf16(
   const int kc = K / gridDim.z;
   const int kbeg = blockIdx.z * kc, nch = kc / 64;
   const int r = lane & 15, q = lane >> 4;
-  int64_t am = m0 + r;
-  if (am >= T) am = T - 1;  // clamped rows feed only outputs that are not stored
-  const uint16_t* ap = x + am * (int64_t)ldx + x_off + kbeg + q * 16;
+  const uint16_t* ap[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) {
+    int64_t am = m0 + mb * 16 + r;
+    if (am >= T) am = T - 1;  // clamped rows feed only outputs that are not stored
+    ap[mb] = x + am * (int64_t)ldx + x_off + kbeg + q * 16;
+  }
 
   // B loader: 64 rows x 16 float4 = 1024 float4, 4 per thread; float4 i of
   // this thread is row id/16, K elements 4(id%16) .. +3
@@ -102,21 +111,35 @@ __global__ __launch_bounds__(256) void k_router_logits_bf16(
     }
   };
 
-  f32x4 acc[4];
+  f32x4 acc[MB][4];
 #pragma unroll
-  for (int j = 0; j < 4; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // x fragments of chunk c + 1 are loaded while chunk c multiplies
-  u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
-  u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 8);
+  u32x4 a0[MB], a1[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) {
+    a0[mb] = *reinterpret_cast<const u32x4*>(ap[mb]);
+    a1[mb] = *reinterpret_cast<const u32x4*>(ap[mb] + 8);
+  }
   bload(0);
   bstore(0);
   __syncthreads();
   for (int c = 0; c < nch; c++) {
     const int buf = c & 1;
-    u32x4 an0 = a0, an1 = a1;
+    u32x4 an0[MB], an1[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+      an0[mb] = a0[mb];
+      an1[mb] = a1[mb];
+    }
     if (c + 1 < nch) {
-      an0 = *reinterpret_cast<const u32x4*>(ap + (c + 1) * 64);
-      an1 = *reinterpret_cast<const u32x4*>(ap + (c + 1) * 64 + 8);
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++) {
+        an0[mb] = *reinterpret_cast<const u32x4*>(ap[mb] + (c + 1) * 64);
+        an1[mb] = *reinterpret_cast<const u32x4*>(ap[mb] + (c + 1) * 64 + 8);
+      }
       bload(c + 1);
     }
 #pragma unroll
@@ -127,27 +150,35 @@ __global__ __launch_bounds__(256) void k_router_logits_bf16(
         const int sw = rl_swz(row);
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(&bs[buf][row * 64 + (((2 * q) ^ sw) * 8)]);
         const u32x4 b1 = *reinterpret_cast<const u32x4*>(&bs[buf][row * 64 + (((2 * q + 1) ^ sw) * 8)]);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
-                                                         __builtin_bit_cast(bf16x8, b0), acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
-                                                         __builtin_bit_cast(bf16x8, b1), acc[j], 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a0[mb]), __builtin_bit_cast(bf16x8, b0), acc[mb][j], 0, 0, 0);
+          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a1[mb]), __builtin_bit_cast(bf16x8, b1), acc[mb][j], 0, 0, 0);
+        }
       }
     if (c + 1 < nch) bstore(buf ^ 1);
-    a0 = an0;
-    a1 = an1;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+      a0[mb] = an0[mb];
+      a1[mb] = an1[mb];
+    }
     __syncthreads();
   }
-  // lane holds C[4 q + e][16 j + r] of its wave's 16 tokens
+  // lane holds C[4 q + e][16 j + r] of each of its token blocks
   float* out = logits + blockIdx.z * part_stride;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int n = n0 + 16 * j + r;
+  for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const int64_t m = m0 + 4 * q + e;
-      if (m < T && n < NL) out[m * ldl + col_off + n] = acc[j][e];
+    for (int j = 0; j < 4; j++) {
+      const int n = n0 + 16 * j + r;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int64_t m = m0 + mb * 16 + 4 * q + e;
+        if (m < T && n < NL) out[m * ldl + col_off + n] = acc[mb][j][e];
+      }
     }
-  }
 }
 
 // fp32 layers: one thread per logit, four interleaved fp32 partial sums.
@@ -249,13 +280,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Marks in sel (bit i = slot i) the K best valid pairs: the K-th largest
-// key th is found bit by bit (a key prefix is kept while at least K keys
-// reach it), every key above th is taken, and the keys equal to th are
-// taken by ascending id until K are.
+// Threshold search of wave_select: the largest th with at least K valid
+// keys >= th, found bit by bit (a key prefix is kept while at least K keys
+// reach it).  Stops early once exactly K keys reach the prefix: those K are
+// then the answer whatever the lower bits.
 template <int V>
-__device__ __forceinline__ uint32_t wave_select(const uint32_t (&key)[V], const int (&id)[V],
-                                                uint32_t valid, int K) {
+__device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[V], uint32_t valid,
+                                                     int K) {
   uint32_t th = 0;
   for (int b = 31; b >= 0; b--) {
     const uint32_t cand = th | (1u << b);
@@ -263,7 +294,44 @@ __device__ __forceinline__ uint32_t wave_select(const uint32_t (&key)[V], const 
 #pragma unroll
     for (int i = 0; i < V; i++) cnt += __popcll(__ballot(((valid >> i) & 1u) && key[i] >= cand));
     if (cnt >= K) th = cand;
+    if (cnt == K) break;
   }
+  return th;
+}
+
+// Two threshold searches in one bit loop (two independent chains of
+// ballots and counts; each stops at its own exact count).
+template <int V>
+__device__ __forceinline__ void select_threshold2(const uint32_t (&k0)[V], uint32_t v0, int K0,
+                                                  uint32_t& th0, const uint32_t (&k1)[V],
+                                                  uint32_t v1, int K1, uint32_t& th1) {
+  th0 = th1 = 0;
+  bool d0 = false, d1 = false;
+  for (int b = 31; b >= 0 && !(d0 && d1); b--) {
+    const uint32_t c0 = th0 | (1u << b), c1 = th1 | (1u << b);
+    int n0 = 0, n1 = 0;
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+      n0 += __popcll(__ballot(((v0 >> i) & 1u) && k0[i] >= c0));
+      n1 += __popcll(__ballot(((v1 >> i) & 1u) && k1[i] >= c1));
+    }
+    if (!d0) {
+      if (n0 >= K0) th0 = c0;
+      d0 = n0 == K0;
+    }
+    if (!d1) {
+      if (n1 >= K1) th1 = c1;
+      d1 = n1 == K1;
+    }
+  }
+}
+
+// Marks in sel (bit i = slot i) the K best valid pairs given the threshold
+// th of select_threshold: every key above th is taken, and the keys equal
+// to th are taken by ascending id until K are.
+template <int V>
+__device__ __forceinline__ uint32_t select_at(const uint32_t (&key)[V], const int (&id)[V],
+                                             uint32_t valid, int K, uint32_t th) {
   uint32_t sel = 0, eq = 0;
   int gt = 0, neq = 0;
 #pragma unroll
@@ -289,6 +357,12 @@ __device__ __forceinline__ uint32_t wave_select(const uint32_t (&key)[V], const 
     }
   }
   return sel;
+}
+
+template <int V>
+__device__ __forceinline__ uint32_t wave_select(const uint32_t (&key)[V], const int (&id)[V],
+                                                uint32_t valid, int K) {
+  return select_at<V>(key, id, valid, K, select_threshold<V>(key, valid, K));
 }
 
 // Position of each selected pair in [0, K): slots in order, lanes in order.
@@ -342,15 +416,14 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
   const float* srow = scores + t * (int64_t)(rows + cols);
-  // step 1: rows then columns
+  // step 1: rows and columns, their two threshold searches in one loop
+  float v2[2][V];
+  uint32_t key2[2][V], valid2[2] = {0u, 0u};
+  int id2[2][V];
+#pragma unroll
   for (int side = 0; side < 2; side++) {
     const int n = side ? cols : rows;
-    const int kk = side ? kcol : krow;
     const float* s = srow + (side ? rows : 0);
-    float v[V];
-    uint32_t key[V];
-    int id[V];
-    uint32_t valid = 0;
 #pragma unroll
     for (int i = 0; i < V; i++) {
       const int e = lane + 64 * i;
@@ -358,20 +431,26 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
       if (e < n) {
         sc = s[e];
         for (int z = 1; z < nparts; z++) sc += s[z * part_stride + e];
-        valid |= 1u << i;
+        valid2[side] |= 1u << i;
       }
-      v[i] = sc;
-      key[i] = order_key(sc);
-      id[i] = e;
+      v2[side][i] = sc;
+      key2[side][i] = order_key(sc);
+      id2[side][i] = e;
     }
-    const uint32_t sel = wave_select<V>(key, id, valid, kk);
+  }
+  uint32_t th2[2];
+  select_threshold2<V>(key2[0], valid2[0], krow, th2[0], key2[1], valid2[1], kcol, th2[1]);
+#pragma unroll
+  for (int side = 0; side < 2; side++) {
+    const uint32_t sel =
+        select_at<V>(key2[side], id2[side], valid2[side], side ? kcol : krow, th2[side]);
     int pos[V];
     wave_positions<V>(sel, pos);
 #pragma unroll
     for (int i = 0; i < V; i++)
       if ((sel >> i) & 1u) {
-        sel_val[wave][side][pos[i]] = v[i];
-        sel_idx[wave][side][pos[i]] = id[i];
+        sel_val[wave][side][pos[i]] = v2[side][i];
+        sel_idx[wave][side][pos[i]] = id2[side][i];
       }
   }
   __builtin_amdgcn_wave_barrier();
@@ -444,9 +523,18 @@ hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, Ro
   p1.ny = (int)cdiv(p1.NL, 64);
   if (p0.ny + p1.ny == 0) return hipSuccess;
   if (dtype == MOE_BF16) {
-    dim3 grid((unsigned)cdiv(T, 64), (unsigned)(p0.ny + p1.ny), (unsigned)splits);
-    hipLaunchKernelGGL(k_router_logits_bf16, grid, dim3(256), 0, st, (const uint16_t*)x, T, ldx,
-                       p0, p1, K, logits, ldl, (int64_t)T * ldl);
+    // 256-token blocks when they alone give every CU a block: the weights'
+    // split is then shared by 4x the tokens
+    const int ny = p0.ny + p1.ny;
+    if (splits == 1 && cdiv(T, 256) * ny >= 256) {
+      dim3 grid((unsigned)cdiv(T, 256), (unsigned)ny, 1);
+      hipLaunchKernelGGL(k_router_logits_bf16<256>, grid, dim3(256), 0, st, (const uint16_t*)x,
+                         T, ldx, p0, p1, K, logits, ldl, (int64_t)T * ldl);
+    } else {
+      dim3 grid((unsigned)cdiv(T, 64), (unsigned)ny, (unsigned)splits);
+      hipLaunchKernelGGL(k_router_logits_bf16<64>, grid, dim3(256), 0, st, (const uint16_t*)x,
+                         T, ldx, p0, p1, K, logits, ldl, (int64_t)T * ldl);
+    }
   } else {
     for (const RouterPart& p : {p0, p1})
       if (p.NL > 0)
