@@ -194,6 +194,90 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
   }
 }
 
+// Small batches (E <= 256, n <= kSmallDispatch): the whole dispatch in one
+// block of 1024 threads -- LDS histogram, scan (offsets, counts), then the
+// stable scatter tile by tile in task order (in-wave ranks from ballots, as
+// in k_radix_scatter), then the tile list when asked.  One launch instead
+// of three: decode-sized batches are bound by launch latency.
+constexpr int kSmallDispatch = 4096;
+
+__global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restrict__ idx,
+                                                         int64_t n, int E, int bits,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ perm,
+                                                         int32_t* __restrict__ inv,
+                                                         TileBuild tb) {
+  __shared__ int32_t cnt[256];
+  __shared__ int32_t run[256];
+  __shared__ int32_t wcnt[16][256];
+  __shared__ int32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int mask = (1 << bits) - 1;
+  if (tid < 256) cnt[tid] = 0;
+  for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += 1024) atomicAdd(&cnt[idx[i] & mask], 1);
+  __syncthreads();
+  // exclusive scan of the 256 digit counts by the first 4 waves
+  if (tid < 256) {
+    const int32_t v = cnt[tid];
+    int32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    cnt[tid] = x - v;  // exclusive within the wave for now
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int32_t pre = 0;
+    for (int ww = 0; ww < w; ww++) pre += wsum[ww];
+    run[tid] = cnt[tid] + pre;
+    if (tid < E) offsets[tid] = run[tid];
+  }
+  if (tid == 0) offsets[E] = (int32_t)n;
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024)
+    counts[e] = (e + 1 < E ? run[e + 1] : (int32_t)n) - run[e];
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = 0; base < n; base += 1024) {
+    const int64_t i = base + tid;
+    const bool valid = i < n;
+    const int dg = valid ? (idx[i] & mask) : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < bits; b++) {
+      const uint64_t bb = __ballot(valid && ((dg >> b) & 1));
+      same &= ((dg >> b) & 1) ? bb : ~bb;
+    }
+    const int rank = __popcll(same & lt_mask);
+    if (valid && rank == 0) wcnt[w][dg] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int32_t pos = run[dg] + rank;
+      for (int ww = 0; ww < w; ww++) pos += wcnt[ww][dg];
+      perm[pos] = (int32_t)i;
+      inv[i] = pos;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      int32_t add = 0;
+#pragma unroll
+      for (int ww = 0; ww < 16; ww++) {
+        add += wcnt[ww][tid];
+        wcnt[ww][tid] = 0;
+      }
+      run[tid] += add;
+    }
+    __syncthreads();
+  }
+  if (tb.tiles)
+    build_tile_list(offsets, tb.E_ffn, tb.n_shared, tb.T, tb.BM, tb.nn1, tb.nn2, tb.tiles,
+                    tb.sched);
+}
+
 // offsets[e] = first sorted position whose expert is >= e, read off the
 // sorted order: position p writes every e in (key(p-1), key(p)] (key(-1) =
 // -1, key(n) = E), so each of offsets[0..E] is written exactly once.  The key
@@ -245,6 +329,13 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
                        (int64_t)E);
     hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)cdiv(E + 1, 256)), dim3(256), 0, st, offsets,
                        0, (int64_t)E + 1);
+    return hipGetLastError();
+  }
+  if (bits <= 8 && n <= kSmallDispatch) {
+    TileBuild none;
+    none.tiles = nullptr;
+    hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024), 0, st, idx, n, E, bits, counts,
+                       offsets, perm, inv_perm, tb ? *tb : none);
     return hipGetLastError();
   }
   if (bits <= 8) {

@@ -202,6 +202,21 @@ __global__ void k_router_logits_f32(const float* __restrict__ x, int64_t T, int 
 }
 
 // ------------------------------------------------------------------------
+// Sum of the K-split partials of one logit, in split order.  All loads are
+// issued before the first add (a load-add chain would pay the memory
+// latency once per split).
+constexpr int kMaxRouterSplits = 16;
+__device__ __forceinline__ float sum_parts(const float* p, int nparts, int64_t stride) {
+  float v[kMaxRouterSplits];
+#pragma unroll
+  for (int z = 0; z < kMaxRouterSplits; z++) v[z] = z < nparts ? p[z * stride] : 0.f;
+  float l = v[0];
+#pragma unroll
+  for (int z = 1; z < kMaxRouterSplits; z++)
+    if (z < nparts) l += v[z];
+  return l;
+}
+
 // Softmax top-k selection, one wave per token.  V = values per lane
 // (E <= 64 V).  Logit l = fl32(dot + bias), plus the gating residual r of
 // the MoE++ page ("Approach": router scores carried over from the previous
@@ -226,8 +241,7 @@ __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ l
     int e = lane + 64 * i;
     float l = -INFINITY;
     if (e < E) {
-      l = row[e];
-      for (int z = 1; z < nparts; z++) l += row[z * part_stride + e];
+      l = sum_parts(row + e, nparts, part_stride);
       if (bias) l = l + bias[e];
       if (residual) l = l + residual[t * E + e];
       if (e < E_ffn) l = tau * l;
@@ -429,8 +443,7 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
       const int e = lane + 64 * i;
       float sc = -INFINITY;
       if (e < n) {
-        sc = s[e];
-        for (int z = 1; z < nparts; z++) sc += s[z * part_stride + e];
+        sc = sum_parts(s + e, nparts, part_stride);
         valid2[side] |= 1u << i;
       }
       v2[side][i] = sc;
@@ -511,7 +524,7 @@ int router_splits(int dtype, int64_t T, int NL, int K) {
   if (dtype != MOE_BF16) return 1;
   const int64_t blocks = cdiv(T, 64) * cdiv(NL, 64);
   int S = 1;
-  while (S < 16 && blocks * S < 512 && K % (64 * 2 * S) == 0) S *= 2;
+  while (S < kMaxRouterSplits && blocks * S < 512 && K % (64 * 2 * S) == 0) S *= 2;
   return S;
 }
 
@@ -570,8 +583,7 @@ __global__ __launch_bounds__(256) void k_logits_out(const float* __restrict__ pa
                                                    float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  float l = part[i];
-  for (int z = 1; z < nparts; z++) l += part[z * part_stride + i];
+  float l = sum_parts(part + i, nparts, part_stride);
   if (bias) l = l + bias[i % E];
   if (residual) l = l + residual[i];
   out[i] = l;
