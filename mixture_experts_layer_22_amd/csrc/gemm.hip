@@ -8,15 +8,16 @@
 //
 // X_e rows are gathered from x through the dispatch permutation while the
 // A tile is loaded.  Shared experts are extra groups whose rows are all
-// tokens in order.
+// tokens in order.  For GEMM1 the B tile holds W_gate rows and the same
+// columns' W_up rows, and each wave's fragments pair gate and up columns, so
+// silu(g)*u is formed in registers and H is written once, in bf16.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A block tile
-// is BM x BN (B rows) x 64 (K) staged through LDS, double buffered; every
-// 16-byte chunk of a 128-byte LDS row is stored at chunk ^ (row & 7) so the
-// MFMA fragment reads of 8 consecutive rows hit distinct banks.  For GEMM1
-// the B tile holds BN/2 W_gate rows and the same BN/2 W_up rows, and each
-// wave's fragments pair gate and up columns, so silu(g)*u is formed in
-// registers and H is written once, in bf16.
+// Three kernels: k_gemm_dl (bf16, groups of 64 rows or more: 8 waves,
+// v_mfma_f32_16x16x32_bf16, a five-stage direct-to-LDS K pipeline; the main
+// path), k_grouped_gemm_bf16 (decode-sized groups: 32-row tiles,
+// v_mfma_f32_32x32x16_bf16, K tiles of 64 double buffered through LDS with
+// 16-byte chunk c of a 128-byte row at c ^ (row & 7)), and
+// k_grouped_gemm_f32 (fp32 layers, plain FMA).
 #include <type_traits>
 
 #include "kernels.h"
