@@ -74,22 +74,26 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int32_t* hist, int64_t l
                                                         int64_t n, int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ offsets,
                                                         TileBuild tb) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
+  __shared__ int32_t wtot[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t per = (len + 1023) / 1024;
   const int64_t lo = tid * per;
   const int64_t hi = lo + per < len ? lo + per : len;
   int32_t s = 0;
   for (int64_t i = lo; i < hi; i++) s += hist[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int32_t v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // exclusive scan of the 1024 thread sums: inside each wave by shuffles,
+  // then across the 16 wave totals
+  int32_t x = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
   }
-  int32_t run = tid ? part[tid - 1] : 0;
+  if (lane == 63) wtot[w] = x;
+  __syncthreads();
+  int32_t run = x - s;
+#pragma unroll
+  for (int ww = 0; ww < 16; ww++) run += ww < w ? wtot[ww] : 0;
   for (int64_t i = lo; i < hi; i++) {
     int32_t v = hist[i];
     hist[i] = run;
