@@ -202,8 +202,10 @@ int32_t moe_dispatch(const moe_dims* dims, const int32_t* topk_idx, int64_t T,
  *             p < offsets[E_ffn]) = FFN_e(x_t) of task perm[p]; rows of
  *             zero-computation tasks are not written.  Product key: float
  *             [T*k]; y[p] = silu(u_e . x_t) of task perm[p].
- *   shared_y  out: layer dtype [n_shared*T, d], row s*T + t = shared expert s
- *             on token t; may be NULL when n_shared == 0. */
+ *   shared_y  out: layer dtype [T, d], row t = the sum of the n_shared shared
+ *             experts on token t (OmniMoE page sec. 2.1 "Shared Dense MLP";
+ *             computed as one SwiGLU of width n_shared * f_shared, fp32
+ *             accumulation, rounded once); may be NULL when n_shared == 0. */
 int32_t moe_expert_ffn(const moe_dims* dims, const moe_weights* w,
                        const void* x, int64_t T, const int32_t* topk_idx,
                        const int32_t* perm, const int32_t* offsets, void* y,
@@ -211,7 +213,7 @@ int32_t moe_expert_ffn(const moe_dims* dims, const moe_weights* w,
                        moe_stream stream);
 
 /* Weighted combine back to token order, deterministic (fixed order, fp32):
- *   out_t = sum_s shared_y[s*T+t] + sum_{j<k} gate[t,j] * c_tj
+ *   out_t = shared_y[t] + sum_{j<k} gate[t,j] * c_tj
  * with c_tj = y[inv_perm[t*k+j]] for FFN experts, 0 / x_t / a*x_t + b*v for
  * zero / copy / constant experts (MoE++ page, "Approach"), and
  * y[inv_perm[t*k+j]] * w_e for atomic experts (OmniMoE page sec. 2.1).

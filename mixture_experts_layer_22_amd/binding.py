@@ -324,7 +324,7 @@ class MoELayer:
             y = torch.empty((max(n, 1), self.cfg.d), dtype=self.act_dtype, device=self.device)
         sy = None
         if self.cfg.n_shared:
-            sy = torch.empty((self.cfg.n_shared * T, self.cfg.d), dtype=self.act_dtype,
+            sy = torch.empty((T, self.cfg.d), dtype=self.act_dtype,
                              device=self.device)
         moe_expert_ffn(self.dims, self.weights, x, T, idx, perm, offsets, y, sy,
                        self.workspace(T), stream)

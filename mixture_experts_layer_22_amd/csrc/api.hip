@@ -105,7 +105,7 @@ Layout make_layout(const moe_dims* d, int64_t T) {
   L.perm = take((size_t)L.n * 4);
   L.inv = take((size_t)L.n * 4);
   L.y = take(is_pk(d) ? (size_t)L.n * 4 : (size_t)L.n * d->d * es);
-  L.sy = take((size_t)d->n_shared * T * d->d * es);
+  L.sy = take(d->n_shared ? (size_t)T * d->d * es : 0);  // the shared experts' sum
   L.total = off;
   return L;
 }
@@ -182,6 +182,12 @@ TileBuild tile_build(const moe_dims* d, int64_t T, void* ws, const Layout& L) {
   tb.BM = L.BM;
   tb.nn1 = gemm_n_ntiles(d->dtype, true, d->n_shared && d->f_shared > N1 ? d->f_shared : N1);
   tb.nn2 = gemm_n_ntiles(d->dtype, false, d->d);
+  // down projection K weights (in units of 64): routed f; the shared group
+  // spans all shared experts, n_shared * f_shared
+  tb.kw_r2 = E_groups && d->f > 0 ? d->f / 64 : 1;
+  tb.kw_s2 = d->n_shared ? d->n_shared * d->f_shared / 64 : 1;
+  tb.cap1 = (int)gemm_blocks_per_xcd(L.BM, L.max_tiles, tb.nn1);
+  tb.cap2 = (int)gemm_blocks_per_xcd(L.BM, L.max_tiles, tb.nn2);
   tb.T = T;
   return tb;
 }
@@ -199,8 +205,7 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   int32_t* ntiles = at<int32_t*>(ws, L.ntiles);
   const TileBuild tb = tile_build(d, T, ws, L);
   if (gemms && !tiles_built)
-    MOE_TRY(launch_build_tiles(offsets, E_groups, d->n_shared, T, L.BM, tb.nn1, tb.nn2, tiles,
-                               ntiles, st));
+    MOE_TRY(launch_build_tiles(tb, offsets, st));
   MOE_TRY(mark(3));
   if (is_pk(d)) {
     MOE_TRY(launch_atomic_h(d->dtype, x, w->atom_u, idx, perm, L.n, d->k, d->d, (float*)y, st));
@@ -224,9 +229,15 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   g1.c_routed = H;
   g1.c_shared = Hs;
   g1.N_routed = E_groups ? d->f : 0;
+  // shared expert s: rows s*f_shared on of [n_shared f_shared, d], writing
+  // columns s*f_shared on of H_shared [T, n_shared f_shared]
   g1.N_shared = d->n_shared ? d->f_shared : 0;
   g1.K_routed = d->d;
   g1.K_shared = d->d;
+  g1.b_ld_shared = d->d;
+  g1.k_seg_shared = d->d;
+  g1.b_seg_shared = d->d;  // one K slice
+  g1.c_ld_shared = (int64_t)d->n_shared * d->f_shared;
   if (gemms) MOE_TRY(launch_grouped_gemm(d->dtype, true, L.BM, g1, L.max_tiles, st));
   MOE_TRY(mark(4));
   GemmArgs g2 = g1;
@@ -242,9 +253,16 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   g2.c_routed = is_pk(d) ? nullptr : y;
   g2.c_shared = shared_y;
   g2.N_routed = E_groups ? d->d : 0;
+  // shared experts: one group, K concatenated; expert s's slice is its own
+  // [d, f_shared] block, so the sum of the shared experts comes out of one
+  // accumulation
   g2.N_shared = d->n_shared ? d->d : 0;
   g2.K_routed = E_groups ? d->f : 0;
-  g2.K_shared = d->n_shared ? d->f_shared : 0;
+  g2.K_shared = d->n_shared ? d->n_shared * d->f_shared : 0;
+  g2.b_ld_shared = d->n_shared ? d->f_shared : 1;
+  g2.k_seg_shared = d->n_shared ? d->f_shared : 1;
+  g2.b_seg_shared = (int64_t)d->d * (d->n_shared ? d->f_shared : 1);
+  g2.c_ld_shared = d->d;
   if (gemms) MOE_TRY(launch_grouped_gemm(d->dtype, false, L.BM, g2, L.max_tiles, st));
   return MOE_OK;
 }
@@ -254,7 +272,7 @@ int32_t do_combine(const moe_dims* d, const moe_weights* w, const void* x, int64
                    const void* shared_y, void* out, hipStream_t st) {
   if (is_pk(d)) {
     MOE_TRY(launch_atomic_combine(d->dtype, w->atom_w, idx, gate, inv, (const float*)y, shared_y,
-                                  d->n_shared, T, d->k, d->d, out, st));
+                                  d->n_shared ? 1 : 0, T, d->k, d->d, out, st));
     return MOE_OK;
   }
   CombineArgs a;
@@ -272,7 +290,7 @@ int32_t do_combine(const moe_dims* d, const moe_weights* w, const void* x, int64
   a.d = d->d;
   a.k = d->k;
   a.E_ffn = d->E_ffn;
-  a.n_shared = d->n_shared;
+  a.n_shared = d->n_shared ? 1 : 0;  // shared_y holds the shared experts' sum
   int ci = 0;
   for (int z = 0; z < d->E - d->E_ffn; z++) {
     a.zc_kind[z] = d->zc_kind[z];

@@ -1,8 +1,10 @@
 // Combine back to token order, and the atomic-expert stage.
 //
-// Combine: out_t = sum_s shared_s(x_t) + sum_{j<k} g_tj * c_tj, accumulated
-// in fp32 in that fixed order and rounded once: a gather (one wave per
-// token), so no atomics and a deterministic result.  c_tj is the expert
+// Combine: out_t = shared(x_t) + sum_{j<k} g_tj * c_tj, accumulated in fp32
+// in that fixed order and rounded once: a gather (one wave per token), so no
+// atomics and a deterministic result.  shared(x_t) is the sum of the shared
+// experts, which the down projection forms as one group (n_shared here is 0
+// or 1 rows).  c_tj is the expert
 // output row of task t*k+j, or for MoE++ zero-computation experts ("MoE++:
 // Accelerating Mixture-of-Experts Methods with Zero-Computation Experts",
 // "Approach"): 0 (zero), x_t (copy), a*x_t + b*v with [a,b] = softmax(W_c x_t)

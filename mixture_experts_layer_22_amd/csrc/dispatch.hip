@@ -104,8 +104,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int32_t* hist, int64_t l
   __syncthreads();
   for (int e = tid; e < E; e += 1024) counts[e] = offsets[e + 1] - offsets[e];
   if (tb.tiles)
-    build_tile_list(offsets, tb.E_ffn, tb.n_shared, tb.T, tb.BM, tb.nn1, tb.nn2, tb.tiles,
-                    tb.sched);
+    build_tile_list(offsets, tb);
 }
 
 __device__ __forceinline__ int radix_digit(const int32_t* idx, int32_t task, int shift, int mask) {
@@ -278,8 +277,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
     __syncthreads();
   }
   if (tb.tiles)
-    build_tile_list(offsets, tb.E_ffn, tb.n_shared, tb.T, tb.BM, tb.nn1, tb.nn2, tb.tiles,
-                    tb.sched);
+    build_tile_list(offsets, tb);
 }
 
 // offsets[e] = first sorted position whose expert is >= e, read off the

@@ -59,7 +59,7 @@ __device__ __forceinline__ const T* a_row(const GemmArgs& a, const TileCtx<SWIGL
     return reinterpret_cast<const T*>(a.a_x) + tok * c.K;
   }
   if (c.shared)
-    return reinterpret_cast<const T*>(a.a_shared) + ((int64_t)c.e * a.T + r) * c.K;
+    return reinterpret_cast<const T*>(a.a_shared) + r * c.K;  // one shared group here
   return reinterpret_cast<const T*>(a.a_routed) + r * c.K;
 }
 
@@ -78,13 +78,14 @@ __device__ __forceinline__ const T* b_row(const GemmArgs& a, const TileCtx<SWIGL
     base = c.shared ? a.b0_shared : a.b0_routed;
   }
   if (n >= c.N) return nullptr;
+  if (c.shared) return reinterpret_cast<const T*>(base) + ((int64_t)c.e * c.N + n) * a.b_ld_shared;
   return reinterpret_cast<const T*>(base) + ((int64_t)c.e * c.N + n) * c.K;
 }
 
 template <typename T, bool SWIGLU>
 __device__ __forceinline__ T* c_row(const GemmArgs& a, const TileCtx<SWIGLU>& c, int i) {
   const int64_t r = c.r0 + i;
-  if (c.shared) return reinterpret_cast<T*>(a.c_shared) + ((int64_t)c.e * a.T + r) * c.N;
+  if (c.shared) return reinterpret_cast<T*>(a.c_shared) + r * a.c_ld_shared + (int64_t)c.e * c.N;
   return reinterpret_cast<T*>(a.c_routed) + r * c.N;
 }
 
@@ -147,12 +148,13 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
   u32x4 ra[CA], rb[CB];
   auto gload = [&](int kt) {
     const int col = kt * BK + lchunk * 8;
+    const int64_t bcol = col + (c.shared ? shared_kseg_delta(args, kt * BK) : 0);
 #pragma unroll
     for (int i = 0; i < CA; i++)
       ra[i] = ap[i] ? *reinterpret_cast<const u32x4*>(ap[i] + col) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < CB; i++)
-      rb[i] = bp[i] ? *reinterpret_cast<const u32x4*>(bp[i] + col) : u32x4{0, 0, 0, 0};
+      rb[i] = bp[i] ? *reinterpret_cast<const u32x4*>(bp[i] + bcol) : u32x4{0, 0, 0, 0};
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -407,11 +409,16 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
     }
     src[i] = p + chunk * 8;
   }
+  // shared group of the down projection: K slices in separate blocks (the
+  // delta is 0 elsewhere)
+  const int64_t seg_step = c.shared ? args.b_seg_shared - args.k_seg_shared : 0;
+  const int seg_tiles = c.shared ? args.k_seg_shared / BK : 1;
   auto copy_one = [&](int t, int stage, int i) {
     const int j = wave + NW * i;
     if (j < CT) {
       const int row0 = j < CA ? j * 16 : RA + (j - CA) * 16;
-      dl_copy16(src[i] + t * BK, lds + stage * STAGE + row0 * BK);
+      const int64_t bdel = (j >= CA && seg_step) ? (int64_t)(t / seg_tiles) * seg_step : 0;
+      dl_copy16(src[i] + t * BK + bdel, lds + stage * STAGE + row0 * BK);
     }
   };
 
@@ -589,10 +596,11 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
 #pragma unroll
       for (int e = 0; e < 4; e++) sa[r][cc * 4 + e] = v[e];
     }
+    const int64_t bk0 = k0 + (c.shared ? shared_kseg_delta(args, k0) : 0);
 #pragma unroll
     for (int q = 0; q < NB / 32; q++) {
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (brow[q]) v = *reinterpret_cast<const f32x4*>(brow[q] + k0 + cc * 4);
+      if (brow[q]) v = *reinterpret_cast<const f32x4*>(brow[q] + bk0 + cc * 4);
 #pragma unroll
       for (int e = 0; e < 4; e++) sb[r + 32 * q][cc * 4 + e] = v[e];
     }
@@ -621,11 +629,8 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
 // Tile list and XCD schedule (the builder itself is in tiles.h, shared with
 // the dispatch scan, which builds them in the same launch for a forward).
 __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ offsets,
-                                                      int E_ffn, int n_shared, int64_t T, int BM,
-                                                      int nn1, int nn2,
-                                                      int4* __restrict__ tiles,
-                                                      int32_t* __restrict__ sched) {
-  build_tile_list(offsets, E_ffn, n_shared, T, BM, nn1, nn2, tiles, sched);
+                                                      TileBuild tb) {
+  build_tile_list(offsets, tb);
 }
 
 // ------------------------------------------------------------------------
@@ -647,11 +652,16 @@ int gemm_n_ntiles(int dtype, bool swiglu, int N) {
   return N > 0 ? (int)cdiv(N, bno) : 1;
 }
 
-hipError_t launch_build_tiles(const int32_t* offsets, int E_ffn,
-                              int n_shared, int64_t T, int BM, int nn1, int nn2, int4* tiles,
-                              int32_t* sched, hipStream_t st) {
-  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, st, offsets, E_ffn, n_shared,
-                     T, BM, nn1, nn2, tiles, sched);
+int64_t gemm_blocks_per_xcd(int BM, int64_t max_tiles, int nn) {
+  // enough for an XCD's share of the items: a range holds about 1/8 of the
+  // cost, and on the 256-row path an item costs 4 to 7 (elsewhere 1); the
+  // schedule clamps any range that would hold more
+  const int64_t W = max_tiles * nn;
+  return (BM == 256 ? cdiv(7 * W, 4 * kXcds) : cdiv(W, kXcds)) + 2;
+}
+
+hipError_t launch_build_tiles(const TileBuild& tb, const int32_t* offsets, hipStream_t st) {
+  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, st, offsets, tb);
   return hipGetLastError();
 }
 
@@ -662,11 +672,7 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a
   if (max_tiles == 0 || Nmax == 0) return hipSuccess;
   a.n_ntiles = gemm_n_ntiles(dtype, swiglu, Nmax);
   a.bm = BM;
-  // enough blocks for the longest XCD range: a range holds about 1/8 of the
-  // cost, and on the 256-row path an item costs 4 to 7 (elsewhere 1)
-  const int64_t W = max_tiles * a.n_ntiles;
-  const int64_t per_xcd = (BM == 256 ? cdiv(7 * W, 4 * kXcds) : cdiv(W, kXcds)) + 2;
-  const unsigned grid = (unsigned)(per_xcd * kXcds);
+  const unsigned grid = (unsigned)(gemm_blocks_per_xcd(BM, max_tiles, a.n_ntiles) * kXcds);
   if (dtype == MOE_F32) {
     if (swiglu)
       hipLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3(grid), dim3(256), 0, st, a);

@@ -23,7 +23,7 @@ struct GemmArgs {
   const int32_t* perm;     // GEMM1 routed rows: token = perm[p] / k
   int k;
   const void* a_routed;    // GEMM2: H rows of routed tasks [*, f]
-  const void* a_shared;    // GEMM2: H rows of shared experts [n_shared*T, f_shared]
+  const void* a_shared;    // GEMM2: H of the shared experts [T, n_shared*f_shared]
   // B operand, [groups, N, K] each
   const void* b0_routed;
   const void* b1_routed;
@@ -32,11 +32,29 @@ struct GemmArgs {
   // C
   void* c_routed;
   void* c_shared;
-  int N_routed, N_shared;  // output columns
+  int N_routed, N_shared;  // output columns (of one shared group)
   int K_routed, K_shared;
+  // Shared experts.  Gated GEMM: one group per expert s (B rows s*f_shared
+  // on of the [n_shared f_shared, d] weights), writing columns s*f_shared
+  // on of H [T, n_shared f_shared].  Down projection: one group (group s = 0)
+  // with K = n_shared f_shared: expert s's K slice is its own [d, f_shared]
+  // block, so the experts' sum comes out of one accumulation.  B row n of
+  // shared group s starts at (s*N + n) * b_ld_shared; K element k lies in
+  // slice k / k_seg_shared, whose block starts b_seg_shared elements after
+  // the previous one; C row r of group s starts at r * c_ld_shared + s*N.
+  int b_ld_shared;
+  int k_seg_shared;
+  int64_t b_seg_shared;
+  int64_t c_ld_shared;
   int n_ntiles;            // N tiles per M tile (set by the launcher)
   int bm;                  // rows per M tile (set by the launcher)
 };
+
+// Element offset of K column kcol of a shared-group B row, beyond kcol
+// itself (0 unless the K slices are separate blocks)
+__device__ __forceinline__ int64_t shared_kseg_delta(const GemmArgs& a, int kcol) {
+  return (int64_t)(kcol / a.k_seg_shared) * (a.b_seg_shared - a.k_seg_shared);
+}
 
 struct CombineArgs {
   const void* x;
@@ -86,6 +104,8 @@ struct TileBuild {
   int4* tiles;
   int32_t* sched;
   int E_ffn, n_shared, BM, nn1, nn2;
+  int kw_r2, kw_s2;  // K weights of the routed and the shared groups in the down projection
+  int cap1, cap2;    // blocks per XCD of the two GEMM launches (gemm_blocks_per_xcd)
   int64_t T;
 };
 hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
@@ -97,10 +117,10 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
 int gemm_tile_rows(int dtype, int64_t tasks, int E_ffn);
 int64_t gemm_max_tiles(int64_t T, int k, int E_ffn, int n_shared, int BM);
 int gemm_n_ntiles(int dtype, bool swiglu, int N);
-hipError_t launch_build_tiles(const int32_t* offsets, int E_ffn,
-                              int n_shared, int64_t T, int BM, int nn1, int nn2, int4* tiles,
-                              int32_t* sched,
-                              hipStream_t st);
+// Blocks per XCD of a GEMM launch over max_tiles tiles of nn items: the
+// schedule never gives an XCD more items than this
+int64_t gemm_blocks_per_xcd(int BM, int64_t max_tiles, int nn);
+hipError_t launch_build_tiles(const TileBuild& tb, const int32_t* offsets, hipStream_t st);
 hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a,
                                int64_t max_tiles, hipStream_t st);
 

@@ -9,37 +9,46 @@ namespace moe {
 // Tile list: routed experts e < E_ffn get ceil(count_e / BM) tiles of
 // sorted positions; shared expert s gets ceil(T / BM) tiles of tokens.  Each
 // tile's descriptor names its whole group: {group, first row, rows, first
-// tile}.
+// tile}.  The gated GEMM runs every tile; the down projection runs the
+// routed tiles and those of shared expert 0, whose group there spans all
+// shared experts' K.
 //
 // Then the XCD schedule of both GEMMs.  The expert GEMMs are bound by the
 // rate at which a CU pulls operand bytes from L2, and a 256-row-path item
 // reads its 256 weight rows whatever its height: timed per block, an item
 // costs about a fixed 3 plus 1 per 64 rows of its variant (4 for 64 rows,
-// 7 for 256).  Tiles of the other paths have one size and cost 1.  XCD x
-// starts at the first item whose cost prefix reaches x/8 of the total.
-// Single block; E_ffn <= 1024.
+// 7 for 256), times its K in the down projection (kw_r2 for the routed
+// groups, kw_s2 for the shared one).  Tiles of the other paths have one
+// size and cost 1, times the same K weights.  XCD x starts at the first
+// item whose cost prefix reaches x/8 of the total; then any range longer
+// than the launch's blocks per XCD is cut back (a cost-balanced range of
+// cheap items can be long), so no item is left without a block.  Single
+// block; E_ffn <= 1024.
 __device__ __forceinline__ int tile_cost(int BM, int rows) {
   return BM == 256 ? (rows + 63) / 64 + 3 : 1;
 }
 
 // Tiles [first, first + n) of one group, all of `full` rows but the last of
-// `last` rows, starting at cost prefix P: writes every XCD boundary that
-// falls in them.  A target t lands in tile i (prefix Pi, cost c) when
-// Pi*nn < t <= (Pi+c)*nn, at item i*nn + ceil((t - Pi*nn) / c).
+// `last` rows, starting at cost prefix P[g] in GEMM g with cost weight w[g]
+// (0: not in that GEMM): writes every XCD boundary that falls in them into
+// bnd[g].  A target t lands in tile i (prefix Pi, cost c) when Pi*nn < t <=
+// (Pi+c)*nn, at item i*nn + ceil((t - Pi*nn) / c).
 __device__ __forceinline__ void place_targets(int first, int n, int full, int last, int BM,
-                                              int64_t P, int64_t total, int nn1, int nn2,
-                                              int32_t* sched) {
-  const uint32_t cf = tile_cost(BM, full), cl = tile_cost(BM, last);
+                                              const int64_t (&P)[2], const int64_t (&total)[2],
+                                              const int (&w)[2], int nn1, int nn2,
+                                              int32_t (*bnd)[kXcds + 1]) {
   // rolled loops: the kernel runs once per layer call on a cold instruction
   // cache, so its code must stay small; offsets inside one group fit in 32
   // bits, so the divisions are 32-bit
 #pragma unroll 1
   for (int g = 0; g < 2; g++) {
+    if (w[g] == 0) continue;
+    const uint32_t cf = tile_cost(BM, full) * w[g], cl = tile_cost(BM, last) * w[g];
     const uint32_t nn = g == 0 ? nn1 : nn2;
-    const int64_t lo = P * nn, hi = (P + (int64_t)(n - 1) * cf + cl) * nn;
+    const int64_t lo = P[g] * nn, hi = (P[g] + (int64_t)(n - 1) * cf + cl) * nn;
 #pragma unroll 1
     for (int x = 1; x < kXcds; x++) {
-      const int64_t tgt = (x * total * nn + kXcds - 1) / kXcds;
+      const int64_t tgt = (x * total[g] * nn + kXcds - 1) / kXcds;
       if (tgt <= lo || tgt > hi) continue;
       // full tiles first, then the last one
       const uint32_t d = (uint32_t)(tgt - lo);  // in [1, hi - lo]
@@ -47,18 +56,19 @@ __device__ __forceinline__ void place_targets(int first, int n, int full, int la
       if (i > (uint32_t)(n - 1)) i = n - 1;
       const uint32_t c = i == (uint32_t)(n - 1) ? cl : cf;
       const uint32_t r = d - i * cf * nn;       // target minus the tile's prefix, >= 1
-      sched[1 + g * (kXcds + 1) + x] = (int32_t)((first + i) * nn + (r + c - 1) / c);
+      bnd[g][x] = (int32_t)((first + i) * nn + (r + c - 1) / c);
     }
   }
 }
 
 // Builds the tile list and the schedule with the calling block's 1024
 // threads (offsets must be visible to the whole block).
-__device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offsets, int E_ffn,
-                                                int n_shared, int64_t T, int BM, int nn1, int nn2,
-                                                int4* __restrict__ tiles,
-                                                int32_t* __restrict__ sched) {
+__device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offsets,
+                                                const TileBuild& tb) {
   __shared__ int32_t wtot[2][16];
+  __shared__ int32_t bnd[2][kXcds + 1];
+  const int E_ffn = tb.E_ffn, n_shared = tb.n_shared, BM = tb.BM;
+  const int64_t T = tb.T;
   const int e = threadIdx.x;
   const int cnt = e < E_ffn ? offsets[e + 1] - offsets[e] : 0;
   const int nt = (cnt + BM - 1) / BM;
@@ -74,6 +84,7 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
     if (lane >= o) { sn += a; sc += b; }
   }
   if (lane == 63) { wtot[0][wv] = sn; wtot[1][wv] = sc; }
+  if (e < 2 * (kXcds + 1)) bnd[e / (kXcds + 1)][e % (kXcds + 1)] = 0;  // targets of an empty list
   __syncthreads();
   int bn = 0, bc = 0, tn = 0, tc = 0;
 #pragma unroll
@@ -89,33 +100,49 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   const int64_t routed_cost = tc;
   if (e < E_ffn) {
     const int base = offsets[e];
-    for (int i = 0; i < nt; i++) tiles[start + i] = make_int4(e, base, cnt, start);
+    for (int i = 0; i < nt; i++) tb.tiles[start + i] = make_int4(e, base, cnt, start);
   }
   const int per_shared = (int)((T + BM - 1) / BM);
   const int shared_last = (int)(T - (int64_t)(per_shared - 1) * BM);
   for (int j = e; j < n_shared * per_shared; j += 1024) {
     const int s = j / per_shared;
-    tiles[routed_total + j] = make_int4(E_ffn + s, 0, (int)T, routed_total + s * per_shared);
+    tb.tiles[routed_total + j] = make_int4(E_ffn + s, 0, (int)T, routed_total + s * per_shared);
   }
-  const int ntot = routed_total + n_shared * per_shared;
   const int64_t cs = per_shared ? (int64_t)(per_shared - 1) * tile_cost(BM, BM) +
                                       tile_cost(BM, shared_last) : 0;
-  const int64_t total = routed_cost + n_shared * cs;
-
-  if (e == 0) {
-    sched[0] = ntot;
-    for (int g = 0; g < 2; g++) {
-      const int nn = g == 0 ? nn1 : nn2;
-      for (int x = 0; x < kXcds; x++) sched[1 + g * (kXcds + 1) + x] = 0;  // targets of an empty list
-      sched[1 + g * (kXcds + 1) + kXcds] = ntot * nn;
-    }
+  const int s2 = n_shared > 0 ? 1 : 0;  // shared groups in the down projection
+  const int64_t total[2] = {routed_cost + n_shared * cs,
+                            routed_cost * tb.kw_r2 + s2 * cs * tb.kw_s2};
+  const int items[2] = {(routed_total + n_shared * per_shared) * tb.nn1,
+                        (routed_total + s2 * per_shared) * tb.nn2};
+  if (e < 2) bnd[e][kXcds] = items[e];
+  __syncthreads();
+  if (e < E_ffn && nt > 0) {
+    const int64_t P[2] = {(int64_t)cstart, (int64_t)cstart * tb.kw_r2};
+    const int w[2] = {1, tb.kw_r2};
+    place_targets(start, nt, BM, last, BM, P, total, w, tb.nn1, tb.nn2, bnd);
+  }
+  if (e < n_shared && per_shared > 0) {
+    const int64_t P[2] = {routed_cost + e * cs, routed_cost * tb.kw_r2};
+    const int w[2] = {1, e == 0 ? tb.kw_s2 : 0};
+    place_targets(routed_total + e * per_shared, per_shared, BM, shared_last, BM, P, total, w,
+                  tb.nn1, tb.nn2, bnd);
   }
   __syncthreads();
-  if (e < E_ffn && nt > 0)
-    place_targets(start, nt, BM, last, BM, cstart, total, nn1, nn2, sched);
-  if (e < n_shared && per_shared > 0)
-    place_targets(routed_total + e * per_shared, per_shared, BM, shared_last, BM,
-                  routed_cost + e * cs, total, nn1, nn2, sched);
+  if (e < 2) {
+    // no range longer than the launch's blocks per XCD: cut the ranges
+    // from the front, then push the boundaries up from the back (the total
+    // is at most 8 caps, so both passes together leave every range <= cap)
+    int32_t* b = bnd[e];
+    const int cap = e == 0 ? tb.cap1 : tb.cap2;
+#pragma unroll 1
+    for (int x = 1; x < kXcds; x++) b[x] = min(b[x], b[x - 1] + cap);
+#pragma unroll 1
+    for (int x = kXcds - 1; x >= 1; x--) b[x] = max(b[x], b[x + 1] - cap);
+#pragma unroll 1
+    for (int x = 0; x <= kXcds; x++) tb.sched[1 + e * (kXcds + 1) + x] = b[x];
+  }
+  if (e == 0) tb.sched[0] = routed_total + n_shared * per_shared;
 }
 
 }  // namespace moe

@@ -79,7 +79,9 @@ def test_small_stagewise(name):
         if Y_ref.shape[0]:
             assert C.max_rel_l2(np_of(y[:Y_ref.shape[0]]), Y_ref) <= tol
         if cfg.n_shared:
-            assert C.max_rel_l2(np_of(sy), SY_ref) <= tol
+            # shared_y is the shared experts' sum
+            SY_sum = SY_ref.reshape(cfg.n_shared, cfg.T, cfg.d).sum(axis=0)
+            assert C.max_rel_l2(np_of(sy), SY_sum) <= tol
 
     out = layer.combine(x, idx, gate, inv, y, sy)
     out_f = layer.forward(x)
