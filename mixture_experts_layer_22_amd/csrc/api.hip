@@ -169,6 +169,12 @@ int32_t do_route(const moe_dims* d, const moe_weights* w, const void* x, int64_t
   return MOE_OK;
 }
 
+// Items of the down projection's shared group (all shared experts' K in one
+// group): dealt to the XCDs outside the cost-balanced ranges
+int64_t down_shared_items(const moe_dims* d, int64_t T, const Layout& L) {
+  return d->n_shared ? cdiv(T, L.BM) * gemm_n_ntiles(d->dtype, false, d->d) : 0;
+}
+
 // The expert GEMMs' tile list build for these dims (tiles == nullptr when
 // the layer has no GEMM).
 TileBuild tile_build(const moe_dims* d, int64_t T, void* ws, const Layout& L) {
@@ -182,12 +188,9 @@ TileBuild tile_build(const moe_dims* d, int64_t T, void* ws, const Layout& L) {
   tb.BM = L.BM;
   tb.nn1 = gemm_n_ntiles(d->dtype, true, d->n_shared && d->f_shared > N1 ? d->f_shared : N1);
   tb.nn2 = gemm_n_ntiles(d->dtype, false, d->d);
-  // down projection K weights (in units of 64): routed f; the shared group
-  // spans all shared experts, n_shared * f_shared
-  tb.kw_r2 = E_groups && d->f > 0 ? d->f / 64 : 1;
-  tb.kw_s2 = d->n_shared ? d->n_shared * d->f_shared / 64 : 1;
   tb.cap1 = (int)gemm_blocks_per_xcd(L.BM, L.max_tiles, tb.nn1);
-  tb.cap2 = (int)gemm_blocks_per_xcd(L.BM, L.max_tiles, tb.nn2);
+  tb.cap2 = (int)(gemm_blocks_per_xcd(L.BM, L.max_tiles, tb.nn2) -
+                  cdiv(down_shared_items(d, T, L), kXcds));
   tb.T = T;
   return tb;
 }
@@ -263,6 +266,8 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   g2.k_seg_shared = d->n_shared ? d->f_shared : 1;
   g2.b_seg_shared = (int64_t)d->d * (d->n_shared ? d->f_shared : 1);
   g2.c_ld_shared = d->d;
+  g2.shared_items = (int)down_shared_items(d, T, L);
+  g2.rev = 1;
   if (gemms) MOE_TRY(launch_grouped_gemm(d->dtype, false, L.BM, g2, L.max_tiles, st));
   return MOE_OK;
 }

@@ -96,12 +96,26 @@ __device__ __forceinline__ T* c_row(const GemmArgs& a, const TileCtx<SWIGLU>& c,
 // tiles of one M tile are consecutive: they share the gathered A rows;
 // consecutive M tiles of one expert share its weights) and cut into 8
 // contiguous ranges of about equal cost, range x going to the blocks of XCD
-// x in order.  Blocks past their XCD's range exit.
+// x.  In the down projection the shared group's items, which run over all
+// shared experts' K and are the longest, follow the ranges: XCD x first
+// takes its equal share of them, items [x S/8, (x+1) S/8), so every XCD
+// starts its long items first and no XCD ends on a run of them; then its
+// range, walked from the end when a.rev is set.  Blocks past both exit.
 __device__ __forceinline__ bool work_item(const GemmArgs& a, int& m_tile, int& n_tile) {
   const int b = blockIdx.x;
   const int x = b % kXcds;
-  const int w = a.xcd_first[x] + b / kXcds;
-  if (w >= a.xcd_first[x + 1]) return false;
+  int j = b / kXcds;
+  int w;
+  const int s0 = (int)((int64_t)x * a.shared_items / kXcds);
+  const int s1 = (int)((int64_t)(x + 1) * a.shared_items / kXcds);
+  if (j < s1 - s0) {
+    w = a.xcd_first[kXcds] + s0 + j;
+  } else {
+    j -= s1 - s0;
+    const int first = a.xcd_first[x], end = a.xcd_first[x + 1];
+    if (first + j >= end) return false;
+    w = a.rev ? end - 1 - j : first + j;
+  }
   m_tile = w / a.n_ntiles;
   n_tile = w - m_tile * a.n_ntiles;
   return true;

@@ -46,6 +46,10 @@ struct GemmArgs {
   int k_seg_shared;
   int64_t b_seg_shared;
   int64_t c_ld_shared;
+  int rev;                 // walk each XCD's item range from its end
+  // items after the ranges' end (the down projection's shared group), dealt
+  // to the XCDs in equal shares and run before their ranges; 0: none
+  int shared_items;
   int n_ntiles;            // N tiles per M tile (set by the launcher)
   int bm;                  // rows per M tile (set by the launcher)
 };
@@ -104,8 +108,9 @@ struct TileBuild {
   int4* tiles;
   int32_t* sched;
   int E_ffn, n_shared, BM, nn1, nn2;
-  int kw_r2, kw_s2;  // K weights of the routed and the shared groups in the down projection
-  int cap1, cap2;    // blocks per XCD of the two GEMM launches (gemm_blocks_per_xcd)
+  // longest XCD range of each GEMM: its blocks per XCD (gemm_blocks_per_xcd)
+  // less the XCD's share of the down projection's shared items
+  int cap1, cap2;
   int64_t T;
 };
 hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,

@@ -13,25 +13,29 @@ namespace moe {
 // routed tiles and those of shared expert 0, whose group there spans all
 // shared experts' K.
 //
-// Then the XCD schedule of both GEMMs.  The expert GEMMs are bound by the
-// rate at which a CU pulls operand bytes from L2, and a 256-row-path item
-// reads its 256 weight rows whatever its height: timed per block, an item
-// costs about a fixed 3 plus 1 per 64 rows of its variant (4 for 64 rows,
-// 7 for 256), times its K in the down projection (kw_r2 for the routed
-// groups, kw_s2 for the shared one).  Tiles of the other paths have one
-// size and cost 1, times the same K weights.  XCD x starts at the first
-// item whose cost prefix reaches x/8 of the total; then any range longer
-// than the launch's blocks per XCD is cut back (a cost-balanced range of
-// cheap items can be long), so no item is left without a block.  Single
-// block; E_ffn <= 1024.
-__device__ __forceinline__ int tile_cost(int BM, int rows) {
-  return BM == 256 ? (rows + 63) / 64 + 3 : 1;
+// Then the XCD schedule: contiguous item ranges of about equal cost, one
+// per XCD, over all items in the gated GEMM and over the routed items in
+// the down projection (whose shared items, the longest, are dealt to the
+// XCDs in equal shares by the kernel itself).  The expert GEMMs are bound
+// by the rate at which a CU pulls operand bytes from L2, and a
+// 256-row-path item reads its 256 weight rows whatever its height: timed
+// per block, an item costs about a fixed base plus 1 per 64 rows of its
+// variant (base 3 in the gated GEMM, 4 in the down projection, whose
+// shorter K leaves the weight reads a larger share).  Tiles of the other
+// paths have one size and cost 1.  XCD x starts at the first item whose
+// cost prefix reaches x/8 of the total; then any range longer than its
+// share of the launch's blocks per XCD is cut back (cap1, cap2), so no item
+// is left without a block.  Single block; E_ffn <= 1024.
+// rows-dependent part of an item's cost, and the base of GEMM g
+__device__ __forceinline__ int tile_units(int BM, int rows) {
+  return BM == 256 ? (rows + 63) / 64 : 0;
 }
+__device__ __forceinline__ int tile_base(int BM, int g) { return BM == 256 ? 3 + g : 1; }
 
 // Tiles [first, first + n) of one group, all of `full` rows but the last of
 // `last` rows, starting at cost prefix P[g] in GEMM g with cost weight w[g]
-// (0: not in that GEMM): writes every XCD boundary that falls in them into
-// bnd[g].  A target t lands in tile i (prefix Pi, cost c) when Pi*nn < t <=
+// (1, or 0: not in that GEMM's ranges): writes every XCD boundary that falls
+// in them into bnd[g].  A target t lands in tile i (prefix Pi, cost c) when Pi*nn < t <=
 // (Pi+c)*nn, at item i*nn + ceil((t - Pi*nn) / c).
 __device__ __forceinline__ void place_targets(int first, int n, int full, int last, int BM,
                                               const int64_t (&P)[2], const int64_t (&total)[2],
@@ -43,7 +47,8 @@ __device__ __forceinline__ void place_targets(int first, int n, int full, int la
 #pragma unroll 1
   for (int g = 0; g < 2; g++) {
     if (w[g] == 0) continue;
-    const uint32_t cf = tile_cost(BM, full) * w[g], cl = tile_cost(BM, last) * w[g];
+    const uint32_t cf = (tile_units(BM, full) + tile_base(BM, g)) * w[g];
+    const uint32_t cl = (tile_units(BM, last) + tile_base(BM, g)) * w[g];
     const uint32_t nn = g == 0 ? nn1 : nn2;
     const int64_t lo = P[g] * nn, hi = (P[g] + (int64_t)(n - 1) * cf + cl) * nn;
 #pragma unroll 1
@@ -73,7 +78,7 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   const int cnt = e < E_ffn ? offsets[e + 1] - offsets[e] : 0;
   const int nt = (cnt + BM - 1) / BM;
   const int last = cnt - (nt - 1) * BM;
-  const int ce = nt ? (nt - 1) * tile_cost(BM, BM) + tile_cost(BM, last) : 0;
+  const int ce = nt ? (nt - 1) * tile_units(BM, BM) + tile_units(BM, last) : 0;
   // inclusive scans of (nt, ce) over the 1024 threads: within each wave by
   // shuffles, then across the 16 wave totals
   const int lane = e & 63, wv = e >> 6;
@@ -95,9 +100,11 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
     tc += b;
   }
   const int start = bn + sn - nt;              // exclusive prefix of tile counts
-  const int cstart = bc + sc - ce;             // exclusive prefix of tile costs
+  const int cstart = bc + sc - ce;             // exclusive prefix of tile row units
   const int routed_total = tn;
-  const int64_t routed_cost = tc;
+  // routed costs before the K weights, per GEMM: row units + base per tile
+  const int64_t routed_cost[2] = {tc + (int64_t)tile_base(BM, 0) * tn,
+                                  tc + (int64_t)tile_base(BM, 1) * tn};
   if (e < E_ffn) {
     const int base = offsets[e];
     for (int i = 0; i < nt; i++) tb.tiles[start + i] = make_int4(e, base, cnt, start);
@@ -108,23 +115,25 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
     const int s = j / per_shared;
     tb.tiles[routed_total + j] = make_int4(E_ffn + s, 0, (int)T, routed_total + s * per_shared);
   }
-  const int64_t cs = per_shared ? (int64_t)(per_shared - 1) * tile_cost(BM, BM) +
-                                      tile_cost(BM, shared_last) : 0;
-  const int s2 = n_shared > 0 ? 1 : 0;  // shared groups in the down projection
-  const int64_t total[2] = {routed_cost + n_shared * cs,
-                            routed_cost * tb.kw_r2 + s2 * cs * tb.kw_s2};
+  const int64_t su = per_shared ? (int64_t)(per_shared - 1) * tile_units(BM, BM) +
+                                      tile_units(BM, shared_last) : 0;
+  const int64_t cs[2] = {su + (int64_t)tile_base(BM, 0) * per_shared,
+                         su + (int64_t)tile_base(BM, 1) * per_shared};
+  // the down projection's ranges hold its routed items only
+  const int64_t total[2] = {routed_cost[0] + n_shared * cs[0], routed_cost[1]};
   const int items[2] = {(routed_total + n_shared * per_shared) * tb.nn1,
-                        (routed_total + s2 * per_shared) * tb.nn2};
+                        routed_total * tb.nn2};
   if (e < 2) bnd[e][kXcds] = items[e];
   __syncthreads();
   if (e < E_ffn && nt > 0) {
-    const int64_t P[2] = {(int64_t)cstart, (int64_t)cstart * tb.kw_r2};
-    const int w[2] = {1, tb.kw_r2};
+    const int64_t P[2] = {cstart + (int64_t)tile_base(BM, 0) * start,
+                          cstart + (int64_t)tile_base(BM, 1) * start};
+    const int w[2] = {1, 1};
     place_targets(start, nt, BM, last, BM, P, total, w, tb.nn1, tb.nn2, bnd);
   }
   if (e < n_shared && per_shared > 0) {
-    const int64_t P[2] = {routed_cost + e * cs, routed_cost * tb.kw_r2};
-    const int w[2] = {1, e == 0 ? tb.kw_s2 : 0};
+    const int64_t P[2] = {routed_cost[0] + e * cs[0], 0};
+    const int w[2] = {1, 0};
     place_targets(routed_total + e * per_shared, per_shared, BM, shared_last, BM, P, total, w,
                   tb.nn1, tb.nn2, bnd);
   }

@@ -221,20 +221,19 @@ def test_fp32_bigger_groups():
 
 
 @pytest.mark.parametrize("T,E,k,f,n_shared,f_shared", [
-    (4096, 2, 1, 2048, 1, 64),   # 256-row path: 18 cheap items fall in the last range
-    (1024, 8, 2, 64, 4, 256),    # 256-row path: 12 cheap routed items in the first range
-    (256, 64, 1, 1024, 1, 64),   # 32-row path: 15 items in the last range
+    (4096, 2, 1, 2048, 1, 64),   # 256-row path: shared items 16x shorter than routed ones
+    (1024, 8, 2, 64, 4, 256),    # 256-row path: shared items 16x longer
+    (256, 64, 1, 1024, 1, 64),   # 32-row path: many small routed groups
 ])
-def test_uneven_down_projection_costs(T, E, k, f, n_shared, f_shared):
-    """The down projection's XCD ranges are balanced by K-weighted cost, so a
-    range of cheap items can hold more items than its XCD has blocks (here
-    more than the 10, 9 and 12 blocks per XCD of these launches, by the
-    schedule's own arithmetic); every item must still run (the ranges are
-    capped at the launch's blocks per XCD)."""
+def test_uneven_down_projection_items(T, E, k, f, n_shared, f_shared):
+    """The down projection balances its routed items over the XCDs by cost
+    and deals the shared group's items (K over all shared experts) to the
+    XCDs in equal shares outside those ranges; every item must run exactly
+    once whatever the two kinds cost."""
     cfg = I.small_variant("deepseek16b").replace(T=T, d=256, E=E, E_ffn=E, k=k, f=f,
                                                  n_shared=n_shared, f_shared=f_shared,
                                                  zipf_s=None, seed=5)
-    say("uneven down-projection costs", T, E, k, f, n_shared, f_shared)
+    say("uneven down-projection items", T, E, k, f, n_shared, f_shared)
     _forward_vs_oracle(cfg, I.make_inputs(cfg))
 
 
