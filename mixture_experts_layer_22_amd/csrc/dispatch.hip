@@ -111,14 +111,20 @@ __device__ __forceinline__ int radix_digit(const int32_t* idx, int32_t task, int
   return (idx[task] >> shift) & mask;
 }
 
-// Per-tile digit histogram: hist[digit * nb + tile].
+// Per-tile digit histogram: hist[digit * nb + tile].  Also sets zero[0..nz)
+// to 0 (the counts that a later kernel accumulates), when given.
 template <int ITEMS>
 __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __restrict__ idx,
                                                               const int32_t* __restrict__ src,
                                                               int64_t n, int shift, int bits,
-                                                              int32_t* __restrict__ hist, int nb) {
+                                                              int32_t* __restrict__ hist, int nb,
+                                                              int32_t* __restrict__ zero,
+                                                              int64_t nz) {
   __shared__ int32_t cnt[256];
   const int tid = threadIdx.x;
+  for (int64_t i = (int64_t)blockIdx.x * kRadixThreads + tid; i < nz;
+       i += (int64_t)gridDim.x * kRadixThreads)
+    zero[i] = 0;
   const int mask = (1 << bits) - 1;
   cnt[tid] = 0;
   __syncthreads();
@@ -286,8 +292,12 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
 // is the id's low `bits` bits -- what the passes sorted on -- clamped to E,
 // which keeps it non-decreasing along the order even for ids outside [0, E)
 // (a caller error: such tasks end up past offsets[E], in no expert's group).
+// counts (zeroed beforehand) gets, for the segment [a, b) of each expert,
+// -a from its first position and +b from its last: integer adds, so the
+// result does not depend on their order.
 __global__ void k_segment_offsets(const int32_t* __restrict__ idx, const int32_t* __restrict__ perm,
-                                  int64_t n, int E, int bits, int32_t* __restrict__ offsets) {
+                                  int64_t n, int E, int bits, int32_t* __restrict__ offsets,
+                                  int32_t* __restrict__ counts) {
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (p > n) return;
   const int32_t mask = (int32_t)((1u << bits) - 1);
@@ -298,12 +308,11 @@ __global__ void k_segment_offsets(const int32_t* __restrict__ idx, const int32_t
   const int lo = p > 0 ? key(p - 1) : -1;
   const int hi = p < n ? key(p) : E;
   for (int e = lo + 1; e <= hi; e++) offsets[e] = (int32_t)p;
-}
-
-__global__ void k_counts_from_offsets(const int32_t* __restrict__ offsets, int E,
-                                      int32_t* __restrict__ counts) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < E) counts[e] = offsets[e + 1] - offsets[e];
+  if (p < n && hi < E) {
+    if (lo < hi) atomicAdd(&counts[hi], -(int32_t)p);
+    const int nx = p + 1 < n ? key(p + 1) : E;
+    if (nx > hi) atomicAdd(&counts[hi], (int32_t)(p + 1));
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -345,7 +354,8 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     const int nb = (int)cdiv(n, kRadixTile);
     int32_t* hist = scratch;
     hipLaunchKernelGGL(k_radix_hist<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
-                       (const int32_t*)nullptr, n, 0, bits, hist, nb);
+                       (const int32_t*)nullptr, n, 0, bits, hist, nb, (int32_t*)nullptr,
+                       (int64_t)0);
     TileBuild none;
     none.tiles = nullptr;
     hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, st, hist,
@@ -369,8 +379,10 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     const bool last = p == passes - 1;
     // ping-pong so that the last pass lands in perm
     int32_t* dst = ((passes - 1 - p) % 2) ? tmp : perm;
+    // the first pass also zeroes counts, which the segment kernel accumulates
     hipLaunchKernelGGL(k_radix_hist<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx, src,
-                       n, shift, pb, hist, nb);
+                       n, shift, pb, hist, nb, p == 0 ? counts : (int32_t*)nullptr,
+                       p == 0 ? (int64_t)E : (int64_t)0);
     hipLaunchKernelGGL(k_digit_scan, dim3(1u << pb), dim3(256), 0, st, hist, nb, totals);
     hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
                        src, n, shift, pb, hist, (const int32_t*)totals, nb, dst,
@@ -378,9 +390,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     src = dst;
   }
   hipLaunchKernelGGL(k_segment_offsets, dim3((unsigned)cdiv(n + 1, 256)), dim3(256), 0, st, idx,
-                     perm, n, E, bits, offsets);
-  hipLaunchKernelGGL(k_counts_from_offsets, dim3((unsigned)cdiv(E, 256)), dim3(256), 0, st,
-                     offsets, E, counts);
+                     perm, n, E, bits, offsets, counts);
   return hipGetLastError();
 }
 

@@ -102,7 +102,7 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   const int start = bn + sn - nt;              // exclusive prefix of tile counts
   const int cstart = bc + sc - ce;             // exclusive prefix of tile row units
   const int routed_total = tn;
-  // routed costs before the K weights, per GEMM: row units + base per tile
+  // routed costs per GEMM: row units + base per tile
   const int64_t routed_cost[2] = {tc + (int64_t)tile_base(BM, 0) * tn,
                                   tc + (int64_t)tile_base(BM, 1) * tn};
   if (e < E_ffn) {
