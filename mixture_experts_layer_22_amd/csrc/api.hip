@@ -267,6 +267,8 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   g2.b_seg_shared = (int64_t)d->d * (d->n_shared ? d->f_shared : 1);
   g2.c_ld_shared = d->d;
   g2.shared_items = (int)down_shared_items(d, T, L);
+  // ranges walked from their ends: timed faster for the down projection
+  // (the MoE++-shaped layer, about 1.5 items per CU, gained 15-20 us)
   g2.rev = 1;
   if (gemms) MOE_TRY(launch_grouped_gemm(d->dtype, false, L.BM, g2, L.max_tiles, st));
   return MOE_OK;
