@@ -1,0 +1,92 @@
+"""Host logic of bench.py, with no GPU: the one-GPU guard, the algorithmic
+work behind the roofline line, and the staleness check of the committed
+traffic record."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from mixture_experts_layer_22_amd import inputs as I  # noqa: E402
+from mixture_experts_layer_22_amd import profiling as P  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def _count_ffn_work(cfg, counts):
+    """The same quantities counted task by task: every routed task and every
+    (token, shared expert) pair runs one SwiGLU of width f (resp. f_shared):
+    two d x f products into H, one f x d product out; each touched expert's
+    three weight matrices are read once."""
+    es = 2 if cfg.dtype == I.DT_BF16 else 4
+    g1 = g2 = 0
+    for e in range(cfg.E_ffn):
+        for _ in range(int(counts[e])):
+            g1 += 2 * (2 * cfg.d * cfg.f)
+            g2 += 2 * cfg.d * cfg.f
+    for _ in range(cfg.T):
+        for _ in range(cfg.n_shared):
+            g1 += 2 * (2 * cfg.d * cfg.f_shared)
+            g2 += 2 * cfg.d * cfg.f_shared
+    w = 0
+    for e in range(cfg.E_ffn):
+        if counts[e]:
+            w += 3 * cfg.d * cfg.f * es
+    w += cfg.n_shared * 3 * cfg.d * cfg.f_shared * es
+    return g1, g2, w
+
+
+@pytest.mark.parametrize("counts", [[3, 0, 5], [0, 0, 8], [4, 4, 0]])
+def test_algorithmic_work_of_the_ffn_layer(counts):
+    # expert 2 is a zero-computation expert: its tasks do no GEMM work
+    cfg = I.LayerConfig(name="t", T=4, d=8, E=3, E_ffn=2, k=2, f=16, n_shared=1, f_shared=8,
+                        zc_kinds=[I.ZC_ZERO])
+    counts = np.array(counts)
+    w = bench.algorithmic_work(cfg, counts)
+    g1, g2, wb = _count_ffn_work(cfg, counts)
+    assert w["expert1_flop"] == g1
+    assert w["expert2_flop"] == g2
+    assert w["weight_bytes"] == wb
+    # the gated GEMM reads its two weight matrices per touched expert and the
+    # tokens, and writes H (bf16)
+    n_ffn = int(counts[:2].sum())
+    touched = int(np.count_nonzero(counts[:2]))
+    h = n_ffn * 16 + 4 * 8
+    assert w["gemm1_bytes"] == 2 * (touched * 2 * 8 * 16 + 2 * 8 * 8 + 4 * 8 + h)
+
+
+def test_algorithmic_work_of_the_atomic_layer():
+    cfg = I.LayerConfig(name="t", T=3, d=16, E=9, E_ffn=9, k=2, f=0, router=I.ROUTER_PRODUCT_KEY,
+                        pk_rows=3, pk_cols=3, pk_k_row=2, pk_k_col=2)
+    counts = np.array([2, 0, 1, 0, 0, 3, 0, 0, 0])  # 6 tasks on 3 experts
+    w = bench.algorithmic_work(cfg, counts)
+    assert w["expert1_flop"] == 2 * 16 * 6 and w["expert2_flop"] == 2 * 16 * 6
+    assert w["weight_bytes"] == 3 * 16 * 2
+    # each touched in-vector and each token once (bf16), one fp32 per task
+    assert w["atomic_h_bytes"] == (3 + 3) * 16 * 2 + 6 * 4
+
+
+def test_traffic_record_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
+    kernel = "k_gemm_dl<true>"
+    rec = {"kernel": kernel, "bytes": 123.0, "source_sha256": P.kernel_source_sha(kernel)}
+    (tmp_path / "traffic_w.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.measured_traffic("w", kernel) == 123.0
+    # another kernel's record, or a record of an older source, is not used
+    assert bench.measured_traffic("w", "k_gemm_dl<false>") is None
+    rec["source_sha256"] = "0" * 64
+    (tmp_path / "traffic_w.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("w", kernel) is None
+    assert bench.measured_traffic("missing", kernel) is None
