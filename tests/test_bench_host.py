@@ -90,3 +90,38 @@ def test_traffic_record_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch
     (tmp_path / "traffic_w.json").write_text(json.dumps(rec))
     assert bench.measured_traffic("w", kernel) is None
     assert bench.measured_traffic("missing", kernel) is None
+
+
+def _counter_csv(path, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for r in rows:
+            f.write(",".join(str(v) for v in r) + "\n")
+
+
+def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
+    """Counters are summed over a dispatch's instances, averaged over the
+    kernel's dispatches, and scaled by what they read for a copy of known
+    size (the largest copy dispatch is the calibration one)."""
+    copy_bytes = 1 << 20
+    # the copy's FETCH_SIZE reads half its bytes, WRITE_SIZE all of them (in KiB)
+    _counter_csv(tmp_path / "cf", [(1, "copyBuffer", "FETCH_SIZE", 256.0),
+                                   (1, "copyBuffer", "FETCH_SIZE", 256.0),
+                                   (2, "copyBuffer", "FETCH_SIZE", 3.0)])
+    _counter_csv(tmp_path / "cw", [(1, "copyBuffer", "WRITE_SIZE", 1024.0)])
+    k = "k_gemm_dl<true>"
+    _counter_csv(tmp_path / "f", [(5, k + "(moe::GemmArgs)", "FETCH_SIZE", 100.0),
+                                  (5, k + "(moe::GemmArgs)", "FETCH_SIZE", 20.0),
+                                  (9, k + "(moe::GemmArgs)", "FETCH_SIZE", 80.0),
+                                  (7, "other", "FETCH_SIZE", 1e9)])
+    _counter_csv(tmp_path / "w", [(5, k + "(moe::GemmArgs)", "WRITE_SIZE", 10.0),
+                                  (9, k + "(moe::GemmArgs)", "WRITE_SIZE", 30.0)])
+    rec = P.traffic_record(k, str(tmp_path / "cf"), str(tmp_path / "cw"), str(tmp_path / "f"),
+                           str(tmp_path / "w"), copy_bytes, copy_kernel="copyBuffer")
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["fetch_bytes"] == 100.0 * 1024 * 2.0   # (120 + 80) / 2 KiB, doubled
+    assert rec["write_bytes"] == 20.0 * 1024
+    assert rec["bytes"] == rec["fetch_bytes"] + rec["write_bytes"]
+    assert rec["dispatches"] == [2, 2]
+    assert rec["source_sha256"] == P.kernel_source_sha(k)
