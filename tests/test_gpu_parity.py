@@ -237,6 +237,64 @@ def test_uneven_down_projection_items(T, E, k, f, n_shared, f_shared):
     _forward_vs_oracle(cfg, I.make_inputs(cfg))
 
 
+def _random_layers(n=16, seed=2024):
+    """Seeded random softmax-router layers within the boundary's limits:
+    both dtypes, both GEMM tile paths (the large ones have over 64 tasks per
+    expert), 0-3 shared experts, zero-computation experts, renorm, tau."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        big = i % 4 == 3
+        E_ffn = int(rng.integers(2, 9)) if big else int(rng.integers(1, 41))
+        n_zc = int(rng.integers(0, 4))
+        E = E_ffn + n_zc
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(600, 1500)) if big else int(rng.integers(1, 400))
+        n_shared = int(rng.integers(0, 4))
+        out.append(I.LayerConfig(
+            name=f"random{i}", T=T, d=int(rng.choice([64, 128, 256])), E=E, E_ffn=E_ffn, k=k,
+            f=int(rng.choice([64, 128, 192, 320])),
+            dtype=I.DT_F32 if rng.random() < 0.2 else I.DT_BF16,
+            n_shared=n_shared, f_shared=int(rng.choice([64, 128, 192])) if n_shared else 0,
+            renorm=bool(rng.random() < 0.5), tau=float(rng.choice([1.0, 0.5])),
+            zipf_s=1.1 if rng.random() < 0.5 else None,
+            zc_kinds=[int(z) for z in rng.integers(0, 3, size=n_zc)], seed=100 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_layers(), ids=lambda c: c.name)
+def test_random_layers(cfg):
+    say("random layer", cfg)
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
+def _random_pk_layers(n=8, seed=2025):
+    """Seeded random product-key layers of atomic experts: grids up to
+    96 x 96, row / column top-k up to 32 (k up to 64), both dtypes, with and
+    without a shared dense SwiGLU."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        rows, cols = int(rng.integers(2, 97)), int(rng.integers(2, 97))
+        kr, kc = int(rng.integers(1, min(rows, 32) + 1)), int(rng.integers(1, min(cols, 32) + 1))
+        k = int(rng.integers(1, min(kr * kc, 64) + 1))
+        n_shared = int(rng.integers(0, 2))
+        out.append(I.LayerConfig(
+            name=f"random_pk{i}", T=int(rng.integers(1, 500)), d=int(rng.choice([128, 256])),
+            E=rows * cols, E_ffn=0, k=k, f=0, router=I.ROUTER_PRODUCT_KEY,
+            pk_rows=rows, pk_cols=cols, pk_k_row=kr, pk_k_col=kc,
+            dtype=I.DT_F32 if rng.random() < 0.25 else I.DT_BF16,
+            n_shared=n_shared, f_shared=int(rng.choice([64, 128])) if n_shared else 0,
+            seed=200 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_pk_layers(), ids=lambda c: c.name)
+def test_random_product_key_layers(cfg):
+    say("random product-key layer", cfg)
+    _forward_vs_oracle(cfg, I.make_inputs(cfg))
+
+
 @pytest.mark.parametrize("name", ["deepseek16b", "atomic-pk", "moepp"])
 def test_deterministic(name):
     cfg = I.small_variant(name).replace(T=300)
