@@ -69,11 +69,10 @@ __global__ __launch_bounds__(256) void k_digit_scan(int32_t* __restrict__ hist, 
 
 // Single-pass dispatch (E <= 256): exclusive scan of the digit-major tile
 // histogram in place, and from it the expert offsets (the scanned value at
-// (e, tile 0)) and counts; then, when asked, the expert GEMMs' tile list.
+// (e, tile 0)) and counts.
 __global__ __launch_bounds__(1024) void k_dispatch_scan(int32_t* hist, int64_t len, int nb, int E,
                                                         int64_t n, int32_t* __restrict__ counts,
-                                                        int32_t* __restrict__ offsets,
-                                                        TileBuild tb) {
+                                                        int32_t* __restrict__ offsets) {
   __shared__ int32_t wtot[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t per = (len + 1023) / 1024;
@@ -103,8 +102,6 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int32_t* hist, int64_t l
   if (tid == 0) offsets[E] = (int32_t)n;
   __syncthreads();
   for (int e = tid; e < E; e += 1024) counts[e] = offsets[e + 1] - offsets[e];
-  if (tb.tiles)
-    build_tile_list(offsets, tb);
 }
 
 __device__ __forceinline__ int radix_digit(const int32_t* idx, int32_t task, int shift, int mask) {
@@ -146,12 +143,19 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __r
 // the tile).  Same-digit lanes of a wave are found with one ballot per key
 // bit.  base[digit, tile] is the scanned histogram, plus the exclusive scan
 // of the digit totals when those are given (multi-pass sorts).  The last
-// pass also writes the inverse permutation.
+// pass also writes the inverse permutation.  With a tile list to build
+// (single-pass dispatch), block nb builds it from the offsets of the scan
+// while the other blocks scatter.
 template <int ITEMS>
 __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ src, int64_t n, int shift,
     int bits, const int32_t* __restrict__ hist_scanned, const int32_t* __restrict__ digit_totals,
-    int nb, int32_t* __restrict__ dst, int32_t* __restrict__ inv) {
+    int nb, int32_t* __restrict__ dst, int32_t* __restrict__ inv,
+    const int32_t* __restrict__ offsets, TileBuild tb) {
+  if (blockIdx.x == nb) {  // launched only when tb.tiles is set
+    build_tile_list(offsets, tb);
+    return;
+  }
   __shared__ int32_t run[256];
   __shared__ int32_t wcnt[kRadixThreads / 64][256];
   __shared__ int32_t wsum[4];
@@ -359,10 +363,13 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     TileBuild none;
     none.tiles = nullptr;
     hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, st, hist,
-                       (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets, tb ? *tb : none);
-    hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
-                       (const int32_t*)nullptr, n, 0, bits, hist, (const int32_t*)nullptr, nb,
-                       perm, inv_perm);
+                       (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets);
+    // an extra block builds the tile list (E <= 256 <= its threads)
+    const bool build = tb && tb->tiles;
+    hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb + (build ? 1 : 0)),
+                       dim3(kRadixThreads), 0, st, idx, (const int32_t*)nullptr, n, 0, bits, hist,
+                       (const int32_t*)nullptr, nb, perm, inv_perm, (const int32_t*)offsets,
+                       build ? *tb : none);
     return hipGetLastError();
   }
   // many experts: 8-bit LSD passes (hist, per-digit scan, scatter), then
@@ -384,9 +391,11 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
                        n, shift, pb, hist, nb, p == 0 ? counts : (int32_t*)nullptr,
                        p == 0 ? (int64_t)E : (int64_t)0);
     hipLaunchKernelGGL(k_digit_scan, dim3(1u << pb), dim3(256), 0, st, hist, nb, totals);
+    TileBuild none;
+    none.tiles = nullptr;
     hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
                        src, n, shift, pb, hist, (const int32_t*)totals, nb, dst,
-                       last ? inv_perm : (int32_t*)nullptr);
+                       last ? inv_perm : (int32_t*)nullptr, (const int32_t*)nullptr, none);
     src = dst;
   }
   hipLaunchKernelGGL(k_segment_offsets, dim3((unsigned)cdiv(n + 1, 256)), dim3(256), 0, st, idx,

@@ -1,5 +1,6 @@
-// Tile list of the expert GEMMs and its XCD schedule, built by one block of
-// 1024 threads (the tile builder kernel, or the dispatch scan of a forward).
+// Tile list of the expert GEMMs and its XCD schedule, built by one block (the
+// tile builder kernel, the small dispatch, or an extra block of the dispatch
+// scatter).
 #pragma once
 
 #include "kernels.h"
@@ -25,7 +26,9 @@ namespace moe {
 // paths have one size and cost 1.  XCD x starts at the first item whose
 // cost prefix reaches x/8 of the total; then any range longer than its
 // share of the launch's blocks per XCD is cut back (cap1, cap2), so no item
-// is left without a block.  Single block; E_ffn <= 1024.
+// is left without a block.  One block of blockDim.x threads, a multiple of
+// 64 with E_ffn <= blockDim.x <= 1024.
+
 // rows-dependent part of an item's cost, and the base of GEMM g
 __device__ __forceinline__ int tile_units(int BM, int rows) {
   return BM == 256 ? (rows + 63) / 64 : 0;
@@ -66,21 +69,21 @@ __device__ __forceinline__ void place_targets(int first, int n, int full, int la
   }
 }
 
-// Builds the tile list and the schedule with the calling block's 1024
-// threads (offsets must be visible to the whole block).
+// Builds the tile list and the schedule with the calling block's threads
+// (offsets must be visible to the whole block).
 __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offsets,
                                                 const TileBuild& tb) {
   __shared__ int32_t wtot[2][16];
   __shared__ int32_t bnd[2][kXcds + 1];
   const int E_ffn = tb.E_ffn, n_shared = tb.n_shared, BM = tb.BM;
   const int64_t T = tb.T;
-  const int e = threadIdx.x;
+  const int e = threadIdx.x, nthreads = blockDim.x, nwaves = nthreads >> 6;
   const int cnt = e < E_ffn ? offsets[e + 1] - offsets[e] : 0;
   const int nt = (cnt + BM - 1) / BM;
   const int last = cnt - (nt - 1) * BM;
   const int ce = nt ? (nt - 1) * tile_units(BM, BM) + tile_units(BM, last) : 0;
-  // inclusive scans of (nt, ce) over the 1024 threads: within each wave by
-  // shuffles, then across the 16 wave totals
+  // inclusive scans of (nt, ce) over the block: within each wave by
+  // shuffles, then across the wave totals
   const int lane = e & 63, wv = e >> 6;
   int sn = nt, sc = ce;
 #pragma unroll
@@ -92,8 +95,8 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   if (e < 2 * (kXcds + 1)) bnd[e / (kXcds + 1)][e % (kXcds + 1)] = 0;  // targets of an empty list
   __syncthreads();
   int bn = 0, bc = 0, tn = 0, tc = 0;
-#pragma unroll
-  for (int w = 0; w < 16; w++) {
+#pragma unroll 1
+  for (int w = 0; w < nwaves; w++) {
     const int a = wtot[0][w], b = wtot[1][w];
     if (w < wv) { bn += a; bc += b; }
     tn += a;
@@ -111,7 +114,7 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   }
   const int per_shared = (int)((T + BM - 1) / BM);
   const int shared_last = (int)(T - (int64_t)(per_shared - 1) * BM);
-  for (int j = e; j < n_shared * per_shared; j += 1024) {
+  for (int j = e; j < n_shared * per_shared; j += nthreads) {
     const int s = j / per_shared;
     tb.tiles[routed_total + j] = make_int4(E_ffn + s, 0, (int)T, routed_total + s * per_shared);
   }
