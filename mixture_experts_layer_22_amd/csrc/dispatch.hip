@@ -21,6 +21,9 @@ namespace moe {
 constexpr int kRadixThreads = 256;
 constexpr int kRadixItems = 4;
 constexpr int kRadixTile = kRadixThreads * kRadixItems;
+// single pass with at most this many tiles: the scatter scans the histogram
+// itself (each block reads all of it), no separate scan launch
+constexpr int kSelfScanTiles = 64;
 
 __global__ void k_fill_i32(int32_t* p, int32_t v, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -142,29 +145,54 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __r
 // an item's destination is base[digit, tile] + (same-digit items earlier in
 // the tile).  Same-digit lanes of a wave are found with one ballot per key
 // bit.  base[digit, tile] is the scanned histogram, plus the exclusive scan
-// of the digit totals when those are given (multi-pass sorts).  The last
-// pass also writes the inverse permutation.  With a tile list to build
-// (single-pass dispatch), block nb builds it from the offsets of the scan
-// while the other blocks scatter.
+// of the digit totals when those are given (multi-pass sorts); or, with
+// scan_self (single pass, few tiles), each block scans the raw histogram
+// itself: its digit's earlier tiles plus all smaller digits.  The last pass
+// also writes the inverse permutation.  Block nb, when launched, is the
+// single pass's extra block: with scan_self it writes the expert offsets and
+// counts (E <= 256 digits), then builds the tile list when asked, while the
+// other blocks scatter.
 template <int ITEMS>
 __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ src, int64_t n, int shift,
-    int bits, const int32_t* __restrict__ hist_scanned, const int32_t* __restrict__ digit_totals,
-    int nb, int32_t* __restrict__ dst, int32_t* __restrict__ inv,
-    const int32_t* __restrict__ offsets, TileBuild tb) {
-  if (blockIdx.x == nb) {  // launched only when tb.tiles is set
-    build_tile_list(offsets, tb);
-    return;
-  }
+    int bits, const int32_t* __restrict__ hist, const int32_t* __restrict__ digit_totals,
+    int nb, int32_t* __restrict__ dst, int32_t* __restrict__ inv, int scan_self, int E,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, TileBuild tb) {
   __shared__ int32_t run[256];
   __shared__ int32_t wcnt[kRadixThreads / 64][256];
   __shared__ int32_t wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int mask = (1 << bits) - 1;
-  int32_t start = tid <= mask ? hist_scanned[(int64_t)tid * nb + blockIdx.x] : 0;
-  if (digit_totals) {
+  int32_t start;
+  if (scan_self) {
+    int32_t tot = 0, pre = 0;
+    if (tid <= mask)
+      for (int b = 0; b < nb; b++) {
+        const int32_t v = hist[(int64_t)tid * nb + b];
+        tot += v;
+        pre += b < (int)blockIdx.x ? v : 0;
+      }
     int32_t unused;
-    start += block256_exclusive(tid <= mask ? digit_totals[tid] : 0, wsum, unused);
+    const int32_t dbase = block256_exclusive(tot, wsum, unused);
+    start = dbase + pre;
+    if (blockIdx.x == nb) {
+      if (tid < E) {
+        offsets[tid] = dbase;
+        counts[tid] = tot;
+      }
+      if (tid == 0) offsets[E] = (int32_t)n;
+      __syncthreads();
+    }
+  } else {
+    start = tid <= mask && (int)blockIdx.x < nb ? hist[(int64_t)tid * nb + blockIdx.x] : 0;
+    if (digit_totals) {
+      int32_t unused;
+      start += block256_exclusive(tid <= mask ? digit_totals[tid] : 0, wsum, unused);
+    }
+  }
+  if (blockIdx.x == nb) {
+    if (tb.tiles) build_tile_list(offsets, tb);
+    return;
   }
   run[tid] = start;
 #pragma unroll
@@ -362,13 +390,17 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
                        (int64_t)0);
     TileBuild none;
     none.tiles = nullptr;
-    hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, st, hist,
-                       (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets);
-    // an extra block builds the tile list (E <= 256 <= its threads)
     const bool build = tb && tb->tiles;
-    hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb + (build ? 1 : 0)),
+    // few tiles: every scatter block scans the histogram itself and an extra
+    // block writes offsets and counts; otherwise one scan block first
+    const int scan_self = nb <= kSelfScanTiles;
+    if (!scan_self)
+      hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, st, hist,
+                         (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets);
+    // the extra block also builds the tile list (E <= 256 <= its threads)
+    hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb + (scan_self || build ? 1 : 0)),
                        dim3(kRadixThreads), 0, st, idx, (const int32_t*)nullptr, n, 0, bits, hist,
-                       (const int32_t*)nullptr, nb, perm, inv_perm, (const int32_t*)offsets,
+                       (const int32_t*)nullptr, nb, perm, inv_perm, scan_self, E, counts, offsets,
                        build ? *tb : none);
     return hipGetLastError();
   }
@@ -395,7 +427,8 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     none.tiles = nullptr;
     hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
                        src, n, shift, pb, hist, (const int32_t*)totals, nb, dst,
-                       last ? inv_perm : (int32_t*)nullptr, (const int32_t*)nullptr, none);
+                       last ? inv_perm : (int32_t*)nullptr, 0, E, (int32_t*)nullptr,
+                       (int32_t*)nullptr, none);
     src = dst;
   }
   hipLaunchKernelGGL(k_segment_offsets, dim3((unsigned)cdiv(n + 1, 256)), dim3(256), 0, st, idx,

@@ -237,6 +237,32 @@ def test_uneven_down_projection_items(T, E, k, f, n_shared, f_shared):
     _forward_vs_oracle(cfg, I.make_inputs(cfg))
 
 
+@pytest.mark.parametrize("T,E,k", [(9000, 16, 8), (20000, 200, 4)])
+def test_dispatch_with_many_tiles(T, E, k):
+    """One-pass dispatch with more than 64 histogram tiles of 1024 tasks
+    (72,000 and 80,000 tasks): the path with a separate scan block, checked
+    bit-exact through the dispatch entry point and end to end on a sample of
+    tokens."""
+    cfg = I.small_variant("deepseek16b").replace(T=T, d=64, E=E, E_ffn=E, k=k, f=64,
+                                                 n_shared=1, f_shared=64, seed=9)
+    inp = I.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    x = x_dev(inp)
+    say("dispatch with many tiles", T, E, k)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
+    out = layer.forward(x, topk_idx=idx, topk_gate=gate)
+    counts, offsets, perm, inv = layer.dispatch(idx)
+    torch.cuda.synchronize()
+    idx_np, gate_np = idx.cpu().numpy(), gate.cpu().numpy()
+    C.check_routing(cfg, inp, idx_np, gate_np)
+    C.check_dispatch(cfg, idx_np, counts.cpu().numpy(), offsets.cpu().numpy(),
+                     perm.cpu().numpy(), inv.cpu().numpy())
+    tok = np.unique(np.r_[0, np.random.default_rng(1).choice(cfg.T, 64), cfg.T - 1])
+    ref, _, _ = O.forward(cfg, inp, idx_np, gate_np.astype(np.float64), tokens=tok)
+    assert C.max_rel_l2(np_of(out)[tok], ref) <= C.out_tol(cfg)
+
+
 def _random_layers(n=16, seed=2024):
     """Seeded random softmax-router layers within the boundary's limits:
     both dtypes, both GEMM tile paths (the large ones have over 64 tasks per
