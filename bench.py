@@ -24,6 +24,7 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (datasheet)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (datasheet)
 METRIC = "MoE layer tokens/sec at 1 GPU; % of bf16 MFMA peak or HBM GB/s"
 COPY_BYTES = 1 << 30
+COLD_BYTES = 512 << 20         # written before each cold step: twice the 256 MB MALL
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -318,6 +319,28 @@ def main():
     for p, name in enumerate(B.PHASES):
         v = [evs[i][p].elapsed_time(evs[i][p + 1]) for i in range(n_traced)]
         phase_us[name] = 1e3 * float(np.mean(v))
+    # per-step spread: steps bracketed one by one, warm, then cold (a 512 MiB
+    # write before each step leaves none of the layer's data in the MALL or
+    # the L2s); the per-step events add a little time of their own
+    def step_times(n, evict=None):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i, (a, b) in enumerate(ev):
+            if evict is not None:
+                evict.fill_(float(i))
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        v = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
+                "p90": float(np.percentile(v, 90)), "steps": n}
+
+    n_dist = max(1, min(args.steps, 50))
+    step_us = step_times(n_dist)
+    scratch = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device=dev)
+    cold_step_us = step_times(max(1, min(args.steps, 20)), scratch)
+    del scratch
     work = algorithmic_work(cfg, counts)
     tokens_per_s = T / (ms_per_step * 1e-3)
 
@@ -361,6 +384,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "phases_us": phase_us,
+        "step_us": step_us,
+        "cold_step_us": cold_step_us,
         "layer_expert_tflops": expert_flop / (ms_per_step * 1e-3) / 1e12,
     }
     if not args.no_cpu_baseline:
