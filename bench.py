@@ -336,6 +336,32 @@ def main():
         return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
                 "p90": float(np.percentile(v, 90)), "steps": n}
 
+    # measured ceilings (libmoe_probes.so): a streaming read of 2 GiB and a
+    # memory-free loop of the GEMM's MFMA, each the best of five runs
+    def best_ms(fn):
+        best = float("inf")
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        return best
+
+    n_rd, rd_blocks = (2 << 30) // 4, 8192
+    rd_buf = torch.ones(n_rd, dtype=torch.float32, device=dev)
+    rd_sums = torch.empty(rd_blocks, dtype=torch.float32, device=dev)
+    read_gbs = n_rd * 4 / (best_ms(lambda: B.moe_probe_stream_read(
+        rd_buf, n_rd, rd_sums, rd_blocks, stream)) * 1e-3) / 1e9
+    del rd_buf, rd_sums
+    mf_iters, mf_blocks = 4096, 512
+    mf_out = torch.empty(mf_blocks, dtype=torch.float32, device=dev)
+    mf_flop = 2.0 * 16 * 16 * 32 * 16 * 8 * mf_iters * mf_blocks
+    mfma_tflops = mf_flop / (best_ms(lambda: B.moe_probe_mfma_loop(
+        mf_iters, mf_out, mf_blocks, stream)) * 1e-3) / 1e12
+    del mf_out
+
     n_dist = max(1, min(args.steps, 50))
     step_us = step_times(n_dist)
     scratch = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device=dev)
@@ -364,6 +390,11 @@ def main():
                 "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS}
     roof["traffic"] = measured_traffic(cfg.name, kern)
+    # beside the datasheet peaks: what this GPU streams and multiplies when
+    # nothing else runs
+    ceiling = {"hbm_read_gbs": read_gbs, "mfma_bf16_tflops": mfma_tflops,
+               "frac_of_measured": roof["achieved"] / (read_gbs if roof["unit"] == "GB/s"
+                                                       else mfma_tflops)}
     expert_flop = work["expert1_flop"] + work["expert2_flop"]
     line = {
         "metric": METRIC,
@@ -383,6 +414,7 @@ def main():
                    "router": "product_key" if cfg.router == 1 else "softmax_topk",
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "measured_ceiling": ceiling,
         "phases_us": phase_us,
         "step_us": step_us,
         "cold_step_us": cold_step_us,

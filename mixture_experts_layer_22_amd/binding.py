@@ -266,6 +266,42 @@ def moe_ablation_atomic_token_centric(dims, w: DeviceWeights, x, T, topk_idx, to
         _ptr(topk_gate), _ptr(out), _stream(stream)), "moe_ablation_atomic_token_centric")
 
 
+# ---------------------------------------------------------------- ceiling probes
+
+PRB_PATH = os.path.join(HERE, "libmoe_probes.so")
+PRB_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_loop"]
+_prb = None
+
+
+def load_probes(path: str = PRB_PATH) -> ctypes.CDLL:
+    """Load the ceiling-probe library (include/moe_probes.h).  Raises if it
+    has not been built."""
+    global _prb
+    if _prb is not None:
+        return _prb
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m mixture_experts_layer_22_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.moe_probe_stream_read.restype = ctypes.c_int32
+    lib.moe_probe_stream_read.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
+    lib.moe_probe_mfma_loop.restype = ctypes.c_int32
+    lib.moe_probe_mfma_loop.argtypes = [ctypes.c_int64, P, ctypes.c_int, P]
+    _prb = lib
+    return lib
+
+
+def moe_probe_stream_read(buf, n, block_sums, blocks, stream=None):
+    _check(load_probes().moe_probe_stream_read(_ptr(buf), int(n), _ptr(block_sums), int(blocks),
+                                               _stream(stream)), "moe_probe_stream_read")
+
+
+def moe_probe_mfma_loop(iters, out, blocks, stream=None):
+    _check(load_probes().moe_probe_mfma_loop(int(iters), _ptr(out), int(blocks), _stream(stream)),
+           "moe_probe_mfma_loop")
+
+
 # ---------------------------------------------------------------- convenience
 
 class MoELayer:

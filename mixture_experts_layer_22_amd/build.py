@@ -20,6 +20,10 @@ ABL_DIR = os.path.join(HERE, "ablation")
 ABL_NAME = "libmoe_ablation.so"
 ABL_PATH = os.path.join(HERE, ABL_NAME)
 ABL_SOURCES = ["token_centric.hip"]
+PRB_DIR = os.path.join(HERE, "probes")
+PRB_NAME = "libmoe_probes.so"
+PRB_PATH = os.path.join(HERE, PRB_NAME)
+PRB_SOURCES = ["probes.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -46,10 +50,12 @@ def _run(cmd):
 
 def build(verbose: bool = False, jobs: int = 5) -> str:
     """Compile every source for gfx950 and link the layer library (returns
-    its path), then the ablation library."""
+    its path), then the ablation and the ceiling-probe libraries."""
     path = _build_lib(CSRC, SOURCES, LIB_NAME, LIB_PATH, verbose, jobs)
     if os.path.isdir(ABL_DIR):
         _build_lib(ABL_DIR, ABL_SOURCES, ABL_NAME, ABL_PATH, verbose, jobs)
+    if os.path.isdir(PRB_DIR):
+        _build_lib(PRB_DIR, PRB_SOURCES, PRB_NAME, PRB_PATH, verbose, jobs)
     return path
 
 

@@ -239,3 +239,37 @@ def test_router_logits_and_residual_rejections(lib):
     # misaligned residual
     assert lib.moe_route(ctypes.byref(dims), ctypes.byref(_weights(router_residual=P + 4)), P, 8,
                          P, P, P, need, None) == B.MOE_ERR_SHAPE
+
+
+PRB_HEADER = os.path.join(ROOT, "include", "moe_probes.h")
+
+
+@pytest.fixture(scope="module")
+def prb():
+    if not os.path.exists(B.PRB_PATH):
+        pytest.fail("libmoe_probes.so is not built (run __graft_entry__.build())")
+    return B.load_probes()
+
+
+def test_probes_export_every_declared_symbol(prb):
+    src = re.sub(r"/\*.*?\*/", "", open(PRB_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    assert set(names) == set(B.PRB_EXPORTED)
+    for n in names:
+        assert hasattr(prb, n), n
+
+
+def test_probes_reject_on_host(prb):
+    P = FAKE
+    read, mfma = prb.moe_probe_stream_read, prb.moe_probe_mfma_loop
+    assert read(None, 16, P, 4, None) == B.MOE_ERR_NULL
+    assert read(P, 16, None, 4, None) == B.MOE_ERR_NULL
+    assert read(P, -4, P, 4, None) == B.MOE_ERR_SHAPE
+    assert read(P, 6, P, 4, None) == B.MOE_ERR_SHAPE        # not a multiple of 4 floats
+    assert read(P + 4, 16, P, 4, None) == B.MOE_ERR_SHAPE   # misaligned
+    assert read(P, 16, P, 0, None) == B.MOE_ERR_SHAPE
+    assert read(P, 16, P, 65537, None) == B.MOE_ERR_SHAPE
+    assert mfma(10, None, 4, None) == B.MOE_ERR_NULL
+    assert mfma(0, P, 4, None) == B.MOE_ERR_SHAPE
+    assert mfma((1 << 19) + 1, P, 4, None) == B.MOE_ERR_SHAPE
+    assert mfma(10, P, 0, None) == B.MOE_ERR_SHAPE
