@@ -15,8 +15,9 @@
 // Three kernels: k_gemm_dl (bf16, groups of 64 rows or more: 8 waves,
 // v_mfma_f32_16x16x32_bf16, a five-stage direct-to-LDS K pipeline; the main
 // path), k_grouped_gemm_bf16 (decode-sized groups: 32-row tiles,
-// v_mfma_f32_32x32x16_bf16, K tiles of 64 double buffered through LDS with
-// 16-byte chunk c of a 128-byte row at c ^ (row & 7)), and
+// v_mfma_f32_32x32x16_bf16, K tiles of 64 in one LDS buffer with the next
+// staged in registers, 16-byte chunk c of a 128-byte row at c ^ (row & 7)),
+// and
 // k_grouped_gemm_f32 (fp32 layers, plain FMA).
 #include <type_traits>
 
@@ -135,8 +136,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
   static_assert(CA >= 1 && CB >= 1 && (NT / 8) % 8 == 0, "tile shape");
   static_assert(!SWIGLU || FN % 2 == 0, "gate/up pairs");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * BK];
+  // one LDS buffer (36 KB): the next K tile waits in registers, and four
+  // blocks fit a CU, so a decode-sized GEMM's items run in one wave with
+  // twice the loads in flight of a double-buffered LDS ring
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[BN * BK];
 
   int tile_id, n_tile;
   if (!work_item(args, tile_id, n_tile)) return;
@@ -170,13 +174,13 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
     for (int i = 0; i < CB; i++)
       rb[i] = bp[i] ? *reinterpret_cast<const u32x4*>(bp[i] + bcol) : u32x4{0, 0, 0, 0};
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&]() {
 #pragma unroll
     for (int i = 0; i < CA; i++)
-      *reinterpret_cast<u32x4*>(&lds_a[buf][(lrow + (NT / 8) * i) * BK + lphys]) = ra[i];
+      *reinterpret_cast<u32x4*>(&lds_a[(lrow + (NT / 8) * i) * BK + lphys]) = ra[i];
 #pragma unroll
     for (int i = 0; i < CB; i++)
-      *reinterpret_cast<u32x4*>(&lds_b[buf][(lrow + (NT / 8) * i) * BK + lphys]) = rb[i];
+      *reinterpret_cast<u32x4*>(&lds_b[(lrow + (NT / 8) * i) * BK + lphys]) = rb[i];
   };
 
   f32x16 acc[FM][FN];
@@ -202,10 +206,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
 
   const int nk = c.K / BK;
   gload(0);
-  sstore(0);
+  sstore();
   __syncthreads();
   for (int kt = 0; kt < nk; kt++) {
-    const int cur = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
     for (int s = 0; s < BK / 16; s++) {
@@ -214,17 +217,20 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
 #pragma unroll
       for (int fm = 0; fm < FM; fm++)
         af[fm] = *reinterpret_cast<const bf16x8*>(
-            &lds_a[cur][((wm * FM + fm) * 32 + frow) * BK + ch]);
+            &lds_a[((wm * FM + fm) * 32 + frow) * BK + ch]);
 #pragma unroll
       for (int fn = 0; fn < FN; fn++)
-        bfr[fn] = *reinterpret_cast<const bf16x8*>(&lds_b[cur][(brow[fn] + frow) * BK + ch]);
+        bfr[fn] = *reinterpret_cast<const bf16x8*>(&lds_b[(brow[fn] + frow) * BK + ch]);
 #pragma unroll
       for (int fm = 0; fm < FM; fm++)
 #pragma unroll
         for (int fn = 0; fn < FN; fn++)
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    if (kt + 1 < nk) {
+      __syncthreads();  // every wave is done with tile kt
+      sstore();
+    }
     __syncthreads();
   }
 
