@@ -1,10 +1,11 @@
 """Benchmark: forward pass of one sparse MoE FFN layer on one MI355X.
 
-Default workload: the DeepSeek-MoE-16B-shaped layer (T=4096 tokens, d=2048,
-64 routed SwiGLU experts top-6 with a Zipf(1.1) router bias, 2 shared
-experts, f=1408, bf16, fp32 router).  A step is one moe_forward over the
-batch (route -> dispatch -> grouped GEMM1+SiLU gate -> grouped GEMM2 ->
-combine), inputs resident in HBM.  Prints one JSON line.
+Default workload: the MoE++-shaped layer, the largest of the five measured
+shapes (T=8192 tokens, d=2048, 16 SwiGLU experts of inner width 5632 plus a
+zero, a copy and two constant experts, top-2, tau=0.75, bf16, fp32 router).
+A step is one moe_forward over the batch (route -> dispatch -> grouped
+GEMM1+SiLU gate -> grouped GEMM2 -> combine), inputs resident in HBM.
+Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline]
@@ -47,60 +48,172 @@ def log(*a):
 
 
 def algorithmic_work(cfg, counts):
-    """Per-launch algorithmic FLOPs of each expert stage and the weight bytes
-    the expert stage must read (each touched expert's weights once)."""
+    """Per-launch algorithmic FLOPs of each expert stage and the bytes each
+    stage kernel must move at the least (each touched expert's weights once,
+    the tokens once, its outputs once)."""
     T, d = cfg.T, cfg.d
+    es = 2 if cfg.dtype == 1 else 4
+    rows_s = T * cfg.n_shared * cfg.f_shared     # shared experts' H columns x tokens
+    sh_w = cfg.n_shared * d * cfg.f_shared * es  # one shared weight matrix set, per matrix
     if cfg.router == 1:
         n = T * cfg.k
         touched = int(np.count_nonzero(counts))
-        es = 2 if cfg.dtype == 1 else 4
-        # k_atomic_h reads each touched expert's in-vector and each token once
-        # and writes one fp32 activation per task
-        return {"expert1_flop": 2.0 * d * n, "expert2_flop": 2.0 * d * n,
-                "weight_bytes": touched * d * es,
-                "atomic_h_bytes": (touched + T) * d * es + n * 4}
+        return {
+            "expert1_flop": 2.0 * d * n + 4.0 * d * rows_s,
+            "expert2_flop": 2.0 * d * n + 2.0 * d * rows_s,
+            "weight_bytes": 2 * touched * d * es + 3 * sh_w,
+            # k_atomic_h: each touched in-vector and each token once, one
+            # fp32 activation per task
+            "atomic_h_bytes": (touched + T) * d * es + n * 4,
+            # k_atomic_combine: each touched out-vector once, the output, and
+            # per task its expert id, gate, sorted position and activation
+            "atomic_combine_bytes": (touched + T * (2 if cfg.n_shared else 1)) * d * es
+                                    + n * 16,
+            "gemm1_flop": 4.0 * d * rows_s,
+            "gemm2_flop": 2.0 * d * rows_s,
+        }
     n_ffn = int(np.sum(counts[:cfg.E_ffn]))
     touched = int(np.count_nonzero(counts[:cfg.E_ffn]))
-    es = 2 if cfg.dtype == 1 else 4
-    rows_f = n_ffn * cfg.f + T * cfg.n_shared * cfg.f_shared
+    rows_f = n_ffn * cfg.f + rows_s
     return {
         "expert1_flop": 4.0 * d * rows_f,
         "expert2_flop": 2.0 * d * rows_f,
-        "weight_bytes": (touched * 3 * d * cfg.f + cfg.n_shared * 3 * d * cfg.f_shared) * es,
+        "gemm1_flop": 4.0 * d * rows_f,
+        "gemm2_flop": 2.0 * d * rows_f,
+        "weight_bytes": touched * 3 * d * cfg.f * es + 3 * sh_w,
         # the gated GEMM's operands: weights of touched experts, the tokens,
         # its output H
         "gemm1_bytes": ((touched * 2 * d * cfg.f + cfg.n_shared * 2 * d * cfg.f_shared) + T * d
-                        + n_ffn * cfg.f + T * cfg.n_shared * cfg.f_shared) * es,
+                        + n_ffn * cfg.f + rows_s) * es,
+        # the down projection: its weights, H, and its outputs Y (routed rows
+        # and the shared experts' sum)
+        "gemm2_bytes": ((touched * d * cfg.f + cfg.n_shared * d * cfg.f_shared) + n_ffn * cfg.f
+                        + rows_s + (n_ffn + (T if cfg.n_shared else 0)) * d) * es,
     }
 
 
-def cpu_baseline(cfg, inp, budget_s=12.0):
-    """Time the CPU oracle on batches of the same workload until ~budget_s of
-    CPU work; returns tokens/s and the sample description."""
-    from oracle import moe_oracle as O
+def stage_kernels(cfg):
+    """(phase, kernel, bound, work key) of each expert-stage kernel the
+    layer launches, in launch order."""
+    out = []
+    if cfg.router == 1:
+        t = "unsigned short" if cfg.dtype == 1 else "float"
+        out.append(("atomic", f"k_atomic_h<{t}>", "hbm", "atomic_h_bytes"))
+        if cfg.n_shared:
+            out.append(("gemm1", "k_gemm_dl<true>", "mfma", "gemm1_flop"))
+            out.append(("gemm2", "k_gemm_dl<false>", "mfma", "gemm2_flop"))
+        out.append(("combine", "k_atomic_combine<%s>" % t, "hbm", "atomic_combine_bytes"))
+        return out
+    if cfg.dtype != 1:
+        return [("gemm1", "k_grouped_gemm_f32<true>", "hbm", "gemm1_bytes"),
+                ("gemm2", "k_grouped_gemm_f32<false>", "hbm", "gemm2_bytes")]
+    if cfg.T * cfg.k / max(cfg.E_ffn, 1) < 64:
+        # decode-sized: the GEMMs stream their weights
+        return [("gemm1", "k_grouped_gemm_bf16<1, 4, 1, 2, true>", "hbm", "gemm1_bytes"),
+                ("gemm2", "k_grouped_gemm_bf16<1, 4, 1, 2, false>", "hbm", "gemm2_bytes")]
+    return [("gemm1", "k_gemm_dl<true>", "mfma", "gemm1_flop"),
+            ("gemm2", "k_gemm_dl<false>", "mfma", "gemm2_flop")]
+
+
+def rooflines(cfg, work, phase_warm, phase_cold):
+    """One roofline record per expert-stage kernel.  An HBM-bound kernel is
+    rated on steps that each follow a 512 MiB write (nothing of the layer in
+    the MALL or the L2s); an MFMA-bound one on warm steps (its weights
+    exceed the MALL anyway); both fractions are kept.  The headline record
+    is the kernel with the longest measured phase."""
+    recs = []
+    for phase, kern, bound, key in stage_kernels(cfg):
+        w_us, c_us = phase_warm[phase], phase_cold[phase]
+        if bound == "hbm":
+            peak, unit, scale = PEAK_HBM_GBS, "GB/s", 1e9
+        else:
+            peak, unit, scale = PEAK_BF16_TFLOPS, "TFLOP/s", 1e12
+        ach_w = work[key] / (w_us * 1e-6) / scale if w_us > 0 else 0.0
+        ach_c = work[key] / (c_us * 1e-6) / scale if c_us > 0 else 0.0
+        ach = ach_c if bound == "hbm" else ach_w
+        recs.append({"bound": bound, "kernel": kern, "phase": phase,
+                     "timing": "cold" if bound == "hbm" else "warm",
+                     "us": c_us if bound == "hbm" else w_us,
+                     "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+                     "frac_warm": ach_w / peak, "frac_cold": ach_c / peak,
+                     "work": work[key], "work_unit": "B" if bound == "hbm" else "FLOP",
+                     "traffic": measured_traffic(cfg.name, kern)})
+    head = max(recs, key=lambda r: r["us"])
+    return head, recs
+
+
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, budget_s=12.0):
+    """Time the CPU oracle, single-threaded and pinned to one host core, on
+    batches of the same workload until ~budget_s of CPU work; returns
+    tokens/s and the sample description.  The oracle runs as it stands
+    (numpy, float64); only its BLAS thread pool is limited to one thread and
+    the process is pinned to one core for the duration."""
+    from oracle import moe_oracle as O
+    from threadpoolctl import threadpool_limits
+    prev = os.sched_getaffinity(0)
+    core = min(prev)
     n_tok = min(cfg.T, 256)
-    done, t0, batches = 0, time.perf_counter(), 0
-    while True:
-        lo = (batches * n_tok) % cfg.T
-        sub = dict(inp)
-        sub["x"] = inp["x"][lo:lo + n_tok]
-        O.forward(cfg.replace(T=sub["x"].shape[0]), sub)
-        done += sub["x"].shape[0]
-        batches += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    done, batches = 0, 0
+    try:
+        os.sched_setaffinity(0, {core})
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            while True:
+                lo = (batches * n_tok) % cfg.T
+                sub = dict(inp)
+                sub["x"] = inp["x"][lo:lo + n_tok]
+                O.forward(cfg.replace(T=sub["x"].shape[0]), sub)
+                done += sub["x"].shape[0]
+                batches += 1
+                el = time.perf_counter() - t0
+                if el >= budget_s:
+                    break
+    finally:
+        os.sched_setaffinity(0, prev)
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host_cpu": host_cpu_model(), "pinned_core": core,
             "sample": f"{batches} batches of {n_tok} tokens of the same layer "
-                      f"({done} tokens, {el:.1f} s), full layer per batch"}
+                      f"({done} tokens, {el:.1f} s), full layer per batch (route, dispatch, "
+                      "experts, combine), numpy float64 with one BLAS thread"}
 
 
 TAUS = (1.0, 0.75, 0.5, 0.25, 0.1)
+
+
+def traced_phases(torch, B, stream, step_traced, n, evict=None):
+    """Mean device time of each phase (us) over n steps bracketed by the
+    library's phase events, recorded on the stream the kernels run on.  With
+    `evict`, a 512 MiB write precedes each step, so none of the layer's data
+    is left in the MALL or the L2s."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_PHASES + 1)]
+           for _ in range(n)]
+    for row in evs:                     # materialise the lazily created events
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(n):
+        if evict is not None:
+            evict.fill_(float(i))
+        step_traced(evs[i])
+    torch.cuda.synchronize()
+    return {name: 1e3 * float(np.mean([evs[i][p].elapsed_time(evs[i][p + 1])
+                                       for i in range(n)]))
+            for p, name in enumerate(B.PHASES)}
+
+
+def expert_stage_us(ph):
+    return ph["atomic"] + ph["gemm1"] + ph["gemm2"]
 
 
 def tau_sweep(args, torch, B, I):
@@ -134,21 +247,10 @@ def tau_sweep(args, torch, B, I):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
-        n_tr = max(1, min(args.steps, 10))
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_PHASES + 1)]
-               for _ in range(n_tr)]
-        for row in evs:
-            for e in row:
-                e.record(stream)
-        torch.cuda.synchronize()
-        for i in range(n_tr):
-            B.moe_forward_traced(layer.dims, layer.weights, x, T, out, ws, evs[i], idx, gate,
-                                 stream)
-        torch.cuda.synchronize()
-        ph = {name: 1e3 * float(np.mean([evs[i][p].elapsed_time(evs[i][p + 1])
-                                          for i in range(n_tr)]))
-              for p, name in enumerate(B.PHASES)}
-        expert_us = ph["expert1"] + ph["expert2"]
+        ph = traced_phases(torch, B, stream, lambda ev: B.moe_forward_traced(
+            layer.dims, layer.weights, x, T, out, ws, ev, idx, gate, stream),
+            max(1, min(args.steps, 10)))
+        expert_us = expert_stage_us(ph)
         if ref_us is None:
             ref_us = expert_us
         print(json.dumps({
@@ -184,19 +286,8 @@ def token_centric_ablation(args, torch, B, I):
                                             stream)
     torch.cuda.synchronize()
     # expert-centric: phases after routing, from traced forwards
-    n_tr = max(1, min(args.steps, 20))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_PHASES + 1)]
-           for _ in range(n_tr)]
-    for row in evs:
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    for i in range(n_tr):
-        B.moe_forward_traced(layer.dims, layer.weights, x, T, out, ws, evs[i], stream=stream)
-    torch.cuda.synchronize()
-    ph = {name: 1e3 * float(np.mean([evs[i][p].elapsed_time(evs[i][p + 1])
-                                      for i in range(n_tr)]))
-          for p, name in enumerate(B.PHASES)}
+    ph = traced_phases(torch, B, stream, lambda ev: B.moe_forward_traced(
+        layer.dims, layer.weights, x, T, out, ws, ev, stream=stream), max(1, min(args.steps, 20)))
     ec_us = sum(v for k, v in ph.items() if k != "route")
     # token-centric: the one kernel
     e0 = torch.cuda.Event(enable_timing=True)
@@ -224,7 +315,9 @@ def main():
     # than after 30); the timed region stays well under a second
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="deepseek16b")
+    ap.add_argument("--workload", default="moepp",
+                    help="moepp (default, the largest layer), deepseek16b, qwen3-decode, "
+                         "atomic-pk, tiny-fp32, or omnimoe (atomic-pk plus a shared MLP)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer three times (counter calibration)")
@@ -274,14 +367,12 @@ def main():
     idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
     gate = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    nph = B.MOE_N_PHASES
 
-    def step(events=None):
-        if events is None:
-            B.moe_forward(layer.dims, layer.weights, x, T, out, ws, idx, gate, stream)
-        else:
-            B.moe_forward_traced(layer.dims, layer.weights, x, T, out, ws, events, idx, gate,
-                                 stream)
+    def step():
+        B.moe_forward(layer.dims, layer.weights, x, T, out, ws, idx, gate, stream)
+
+    def step_traced(events):
+        B.moe_forward_traced(layer.dims, layer.weights, x, T, out, ws, events, idx, gate, stream)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -303,25 +394,17 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # phase breakdown: further steps bracketed by the library's phase events
-    # (recorded on the stream the kernels run on; the markers add a little
-    # time of their own, so these steps are not part of the timed region)
+    # (the markers add a little time of their own, so these steps are not
+    # part of the timed region), warm and cold
     n_traced = max(1, min(args.steps, 20))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)]
-           for _ in range(n_traced)]
-    for row in evs:                     # materialise the lazily created events
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    for i in range(n_traced):
-        step(evs[i])
-    torch.cuda.synchronize()
-    phase_us = {}
-    for p, name in enumerate(B.PHASES):
-        v = [evs[i][p].elapsed_time(evs[i][p + 1]) for i in range(n_traced)]
-        phase_us[name] = 1e3 * float(np.mean(v))
+    log(f"[bench] traced steps {n_traced} warm, {n_traced} cold")
+    phase_us = traced_phases(torch, B, stream, step_traced, n_traced)
+    scratch = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device=dev)
+    phase_cold_us = traced_phases(torch, B, stream, step_traced, n_traced, scratch)
+
     # per-step spread: steps bracketed one by one, warm, then cold (a 512 MiB
-    # write before each step leaves none of the layer's data in the MALL or
-    # the L2s); the per-step events add a little time of their own
+    # write before each step); the per-step events add a little time of
+    # their own
     def step_times(n, evict=None):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
@@ -336,6 +419,10 @@ def main():
         return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
                 "p90": float(np.percentile(v, 90)), "steps": n}
 
+    step_us = step_times(max(1, min(args.steps, 50)))
+    cold_step_us = step_times(max(1, min(args.steps, 20)), scratch)
+    del scratch
+
     # measured ceilings (libmoe_probes.so): a streaming read of 2 GiB and a
     # memory-free loop of the GEMM's MFMA, each the best of five runs
     def best_ms(fn):
@@ -349,6 +436,7 @@ def main():
             best = min(best, a.elapsed_time(b))
         return best
 
+    log("[bench] ceilings")
     n_rd, rd_blocks = (2 << 30) // 4, 8192
     rd_buf = torch.ones(n_rd, dtype=torch.float32, device=dev)
     rd_sums = torch.empty(rd_blocks, dtype=torch.float32, device=dev)
@@ -362,34 +450,9 @@ def main():
         mf_iters, mf_out, mf_blocks, stream)) * 1e-3) / 1e12
     del mf_out
 
-    n_dist = max(1, min(args.steps, 50))
-    step_us = step_times(n_dist)
-    scratch = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device=dev)
-    cold_step_us = step_times(max(1, min(args.steps, 20)), scratch)
-    del scratch
     work = algorithmic_work(cfg, counts)
     tokens_per_s = T / (ms_per_step * 1e-3)
-
-    if cfg.router == 1:
-        # atomic layer: the expert stage is bound by HBM
-        kern = f"k_atomic_h<{'unsigned short' if cfg.dtype == 1 else 'float'}>"
-        ach = work["atomic_h_bytes"] / (phase_us["expert1"] * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": kern, "achieved": ach, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
-    elif T * cfg.k / max(cfg.E_ffn, 1) < 64 or cfg.dtype != 1:
-        # decode-sized (and fp32) layers: the gated GEMM streams its weights
-        kern = "k_grouped_gemm_bf16<1, 4, 1, 2, true>" if cfg.dtype == 1 else \
-            "k_grouped_gemm_f32<true>"
-        ach = work["gemm1_bytes"] / (phase_us["expert1"] * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": kern, "achieved": ach, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
-    else:
-        kern = "k_gemm_dl<true>"
-        ach = work["expert1_flop"] / (phase_us["expert1"] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": kern + " (gated GEMM + SiLU)",
-                "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS}
-    roof["traffic"] = measured_traffic(cfg.name, kern)
+    roof, stages = rooflines(cfg, work, phase_us, phase_cold_us)
     # beside the datasheet peaks: what this GPU streams and multiplies when
     # nothing else runs
     ceiling = {"hbm_read_gbs": read_gbs, "mfma_bf16_tflops": mfma_tflops,
@@ -410,12 +473,14 @@ def main():
         "dtype": "bf16" if cfg.dtype == 1 else "f32",
         "data": "synthetic (seeded N(0,1/sqrt(fan_in)) weights, N(0,1) tokens)",
         "config": {"workload": cfg.name, "T": T, "d": cfg.d, "E": cfg.E, "E_ffn": cfg.E_ffn,
-                   "k": cfg.k, "f": cfg.f, "n_shared": cfg.n_shared,
+                   "k": cfg.k, "f": cfg.f, "n_shared": cfg.n_shared, "f_shared": cfg.f_shared,
                    "router": "product_key" if cfg.router == 1 else "softmax_topk",
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "roofline_stages": stages,
         "measured_ceiling": ceiling,
         "phases_us": phase_us,
+        "phases_cold_us": phase_cold_us,
         "step_us": step_us,
         "cold_step_us": cold_step_us,
         "layer_expert_tflops": expert_flop / (ms_per_step * 1e-3) / 1e12,

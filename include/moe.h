@@ -235,11 +235,12 @@ int32_t moe_forward(const moe_dims* dims, const moe_weights* w, const void* x,
                     moe_stream stream);
 
 /* Number of phases moe_forward_traced marks with events. */
-#define MOE_N_PHASES 6
+#define MOE_N_PHASES 7
 
-/* moe_forward, plus timing marks for profiling the phases of the pass
- * (route, dispatch, tile list, expert stage 1 = grouped GEMM1 or atomic
- * activations, expert stage 2 = grouped GEMM2, combine).
+/* moe_forward, plus timing marks for profiling the phases of the pass:
+ * 0 route, 1 dispatch, 2 tile list of the expert GEMMs, 3 atomic-expert
+ * activations (product-key layers), 4 gated GEMM + SiLU (grouped GEMM1,
+ * routed and shared experts), 5 down projection (grouped GEMM2), 6 combine.
  *   events  NULL, or MOE_N_PHASES + 1 caller-created hipEvent_t handles;
  *           events[i] is recorded on `stream` just before phase i is
  *           enqueued and events[MOE_N_PHASES] after the last one, so

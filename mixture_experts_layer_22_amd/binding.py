@@ -29,8 +29,8 @@ MOE_MAX_ZC = 8
 EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route", "moe_router_logits",
             "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
             "moe_forward_traced"]
-MOE_N_PHASES = 6
-PHASES = ["route", "dispatch", "tiles", "expert1", "expert2", "combine"]
+MOE_N_PHASES = 7
+PHASES = ["route", "dispatch", "tiles", "atomic", "gemm1", "gemm2", "combine"]
 
 
 class MoeError(RuntimeError):

@@ -213,6 +213,7 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   if (is_pk(d)) {
     MOE_TRY(launch_atomic_h(d->dtype, x, w->atom_u, idx, perm, L.n, d->k, d->d, (float*)y, st));
   }
+  MOE_TRY(mark(4));
   void* H = at<void*>(ws, L.h);
   void* Hs = at<void*>(ws, L.hs);
   GemmArgs g1;
@@ -242,7 +243,7 @@ int32_t do_experts(const moe_dims* d, const moe_weights* w, const void* x, int64
   g1.b_seg_shared = d->d;  // one K slice
   g1.c_ld_shared = (int64_t)d->n_shared * d->f_shared;
   if (gemms) MOE_TRY(launch_grouped_gemm(d->dtype, true, L.BM, g1, L.max_tiles, st));
-  MOE_TRY(mark(4));
+  MOE_TRY(mark(5));
   GemmArgs g2 = g1;
   g2.xcd_first = ntiles + 1 + (kXcds + 1);
   g2.a_x = nullptr;
@@ -461,9 +462,9 @@ int32_t moe_forward_traced(const moe_dims* dims, const moe_weights* w, const voi
   if ((s = do_experts(dims, w, x, T, idx, perm, offsets, y, sy, ws, L, st, events, fused)) !=
       MOE_OK)
     return s;
-  MOE_TRY(mark(5));
-  if ((s = do_combine(dims, w, x, T, idx, gate, inv, y, sy, out, st)) != MOE_OK) return s;
   MOE_TRY(mark(6));
+  if ((s = do_combine(dims, w, x, T, idx, gate, inv, y, sy, out, st)) != MOE_OK) return s;
+  MOE_TRY(mark(7));
   return MOE_OK;
 }
 

@@ -18,6 +18,10 @@ Workloads (sizes from the five layer shapes this library is measured on):
 * ``atomic-pk``      T=8192, d=1024, 256x256 atomic experts behind a
                      Cartesian-product router (the OmniMoE page, sec. 2.1-2.2),
                      16+16 row/column keys -> 256 candidates -> top-32, bf16.
+* ``omnimoe``        the atomic-pk layer plus the always-on shared dense MLP
+                     the OmniMoE page pairs it with (sec. 2, 2.1 "Shared Dense
+                     MLP"): one SwiGLU of inner width 4096 = 4d (the page
+                     gives no width; 4d is the usual transformer MLP width).
 
 Recipe: ``numpy.random.Generator(PCG64(seed))``; draws in the order x; router
 (R, or K_r then K_c); per FFN expert W_gate, W_up, W_down; shared experts
@@ -94,11 +98,17 @@ def _base_configs() -> Dict[str, LayerConfig]:
             name="atomic-pk", T=8192, d=1024, E=65536, E_ffn=0, k=32, f=0,
             router=ROUTER_PRODUCT_KEY, pk_rows=256, pk_cols=256,
             pk_k_row=16, pk_k_col=16, seed=1004),
+        "omnimoe": LayerConfig(
+            name="omnimoe", T=8192, d=1024, E=65536, E_ffn=0, k=32, f=0,
+            router=ROUTER_PRODUCT_KEY, pk_rows=256, pk_cols=256,
+            pk_k_row=16, pk_k_col=16, n_shared=1, f_shared=4096, seed=1005),
     }
 
 
 CONFIGS: Dict[str, LayerConfig] = _base_configs()
 CONFIG_ORDER = ["tiny-fp32", "deepseek16b", "qwen3-decode", "moepp", "atomic-pk"]
+# widened workloads beyond the five measured shapes
+EXTRA_ORDER = ["omnimoe"]
 
 
 def make_residual(cfg: LayerConfig, seed: int, scale: float = 1.0) -> np.ndarray:
@@ -127,6 +137,9 @@ def small_variant(name: str, seed: int = 7) -> LayerConfig:
     if name == "atomic-pk":
         return c.replace(T=301, d=128, E=32 * 32, pk_rows=32, pk_cols=32,
                          pk_k_row=8, pk_k_col=8, k=12, seed=seed)
+    if name == "omnimoe":
+        return c.replace(T=301, d=128, E=32 * 32, pk_rows=32, pk_cols=32,
+                         pk_k_row=8, pk_k_col=8, k=12, f_shared=512, seed=seed)
     raise KeyError(name)
 
 

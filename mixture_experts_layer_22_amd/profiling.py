@@ -4,6 +4,8 @@
     python -m mixture_experts_layer_22_amd.profiling traffic --kernel NAME
            --copy-fetch DIR --copy-write DIR --fetch DIR --write DIR
            [--copy-bytes N] [--out FILE] [--cmd CMD]
+    python -m mixture_experts_layer_22_amd.profiling counters DIR [DIR ...]
+           --kernel NAME [--kernel NAME ...] [--out FILE] [--cmd CMD]
 
 `stats` turns a `--kernel-trace --stats` run (CSV output) into a short text
 table (with the bench line's phase times, when the run's log is given).  `traffic` turns two counter runs of a workload (FETCH_SIZE, then
@@ -11,6 +13,13 @@ WRITE_SIZE) into HBM bytes per launch of one kernel, each scaled by what the
 same counter reads for a plain device copy of known size (the copy moves
 copy_bytes in and copy_bytes out), and writes a JSON record that bench.py
 reports as roofline.traffic while the kernel source is unchanged.
+`counters` turns one or more `--pmc` runs into a table of every collected
+counter per dispatch of each named kernel (mean over its dispatches), with
+MFMA-busy and LDS-conflict ratios derived from them.  The bench's MFMA
+ceiling probe (k_mfma_loop, a loop of independent MFMA chains that reaches
+about 0.95 of the bf16 peak) runs in the same process, so its own
+SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES ratio calibrates what a busy
+MFMA pipe reads on this GPU.
 """
 from __future__ import annotations
 
@@ -32,6 +41,7 @@ KERNEL_SOURCES = {
     "k_grouped_gemm_bf16": "gemm.hip",
     "k_grouped_gemm_f32": "gemm.hip",
     "k_atomic_h": "combine.hip",
+    "k_atomic_combine": "combine.hip",
 }
 
 
@@ -103,6 +113,55 @@ def traffic_record(kernel, copy_fetch, copy_write, fetch, write, copy_bytes, cop
     }
 
 
+def counters_by_kernel(run_dirs, kernels):
+    """{kernel: {counter: mean per dispatch}} over the runs' counter CSVs."""
+    out = {k: {} for k in kernels}
+    for d in run_dirs:
+        rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+        names = sorted({r["Counter_Name"] for r in rows})
+        for k in kernels:
+            for c in names:
+                try:
+                    v, n = counter_per_dispatch(d, c, k)
+                except ValueError:
+                    continue
+                out[k][c] = v
+                out[k].setdefault("_dispatches", n)
+    return out
+
+
+def counters_table(run_dirs, kernels, probe="k_mfma_loop"):
+    data = counters_by_kernel(run_dirs, kernels + [probe])
+    names = sorted({c for k in data for c in data[k] if not c.startswith("_")})
+    lines = ["per dispatch, mean over dispatches (counters summed over their instances)", ""]
+    lines.append(f"{'counter':34s} " + " ".join(f"{k[:22]:>24s}" for k in kernels + [probe]))
+    for c in names:
+        lines.append(f"{c:34s} " + " ".join(
+            f"{data[k].get(c, float('nan')):24.4g}" for k in kernels + [probe]))
+
+    def ratio(k, a, b):
+        v = data[k]
+        return v[a] / v[b] if a in v and b in v and v[b] else None
+
+    p_busy = ratio(probe, "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES")
+    lines.append("")
+    for k in kernels:
+        r = ratio(k, "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES")
+        if r is not None:
+            rel = f", {r / p_busy:.3f} of the MFMA probe's" if p_busy else ""
+            lines.append(f"{k}: MFMA busy / SQ busy = {r:.4f}{rel}")
+        lc = ratio(k, "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE") or \
+            ratio(k, "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES")
+        if lc is not None:
+            lines.append(f"{k}: LDS bank-conflict cycles per LDS-active (or SQ-busy) cycle = {lc:.4f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in data[k]:
+            lines.append(f"{k}: bf16 MFMA FLOPs issued (MOPS x 512) = "
+                         f"{data[k]['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g}")
+    if p_busy:
+        lines.append(f"{probe}: MFMA busy / SQ busy = {p_busy:.4f}")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -121,6 +180,11 @@ def main(argv=None):
     t.add_argument("--copy-kernel", default="copy")
     t.add_argument("--out")
     t.add_argument("--cmd", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--out")
+    c.add_argument("--cmd", default="")
     a = ap.parse_args(argv)
     if a.cmd_name == "stats":
         text = stats_table(a.dir)
@@ -131,6 +195,10 @@ def main(argv=None):
                     ph = ", ".join(f"{k} {v:.1f}" for k, v in rec["phases_us"].items())
                     text += (f"\n\nbench line of the same run: {rec['ms_per_step'] * 1e3:.1f} us per step; "
                              f"phases (us, HIP events): {ph}")
+        if a.cmd:
+            text = f"command: {a.cmd}\n\n{text}\n"
+    elif a.cmd_name == "counters":
+        text = counters_table(a.dirs, a.kernel)
         if a.cmd:
             text = f"command: {a.cmd}\n\n{text}\n"
     else:

@@ -73,9 +73,51 @@ def test_algorithmic_work_of_the_atomic_layer():
     counts = np.array([2, 0, 1, 0, 0, 3, 0, 0, 0])  # 6 tasks on 3 experts
     w = bench.algorithmic_work(cfg, counts)
     assert w["expert1_flop"] == 2 * 16 * 6 and w["expert2_flop"] == 2 * 16 * 6
-    assert w["weight_bytes"] == 3 * 16 * 2
+    # both tables' touched rows (in- and out-vectors)
+    assert w["weight_bytes"] == 2 * 3 * 16 * 2
     # each touched in-vector and each token once (bf16), one fp32 per task
     assert w["atomic_h_bytes"] == (3 + 3) * 16 * 2 + 6 * 4
+    # each touched out-vector once, the output once, 16 B of metadata per task
+    assert w["atomic_combine_bytes"] == (3 + 3) * 16 * 2 + 6 * 16
+    assert w["gemm1_flop"] == 0 and w["gemm2_flop"] == 0
+    # with a shared SwiGLU of width 8: its GEMMs over all 3 tokens, its three
+    # weight matrices once, and the combine reads the shared row per token
+    ws = bench.algorithmic_work(cfg.replace(n_shared=1, f_shared=8), counts)
+    assert ws["gemm1_flop"] == 3 * 2 * (2 * 16 * 8) and ws["gemm2_flop"] == 3 * 2 * 16 * 8
+    assert ws["weight_bytes"] == 2 * 3 * 16 * 2 + 3 * 16 * 8 * 2
+    assert ws["atomic_combine_bytes"] == (3 + 2 * 3) * 16 * 2 + 6 * 16
+
+
+def _phases(**kw):
+    ph = dict.fromkeys(["route", "dispatch", "tiles", "atomic", "gemm1", "gemm2", "combine"], 0.0)
+    ph.update(kw)
+    return ph
+
+
+def test_roofline_picks_the_longest_stage_and_rates_hbm_kernels_cold():
+    """The headline record is the stage kernel with the longest phase;
+    HBM-bound kernels are rated on cold steps, MFMA-bound ones on warm."""
+    atom = I.CONFIGS["atomic-pk"]
+    work = {"atomic_h_bytes": 100e9, "atomic_combine_bytes": 50e9}
+    head, recs = bench.rooflines(atom, work, _phases(atomic=1.0, combine=1.5),
+                                 _phases(atomic=4.0, combine=2.0))
+    assert [r["kernel"] for r in recs] == ["k_atomic_h<unsigned short>",
+                                          "k_atomic_combine<unsigned short>"]
+    assert head["kernel"] == "k_atomic_h<unsigned short>" and head["timing"] == "cold"
+    assert head["achieved"] == 100e9 / 4e-6 / 1e9 and head["frac_warm"] == 100e9 / 1e-6 / 1e9 / 8000
+    moepp = I.CONFIGS["moepp"]
+    head, recs = bench.rooflines(moepp, {"gemm1_flop": 2e12, "gemm2_flop": 1e12},
+                                 _phases(gemm1=2.0e6, gemm2=1.5e6), _phases(gemm1=9e6, gemm2=1e6))
+    assert head["kernel"] == "k_gemm_dl<true>" and head["bound"] == "mfma"
+    assert head["achieved"] == 2e12 / 2.0 / 1e12 and head["timing"] == "warm"
+    dec = I.CONFIGS["qwen3-decode"]
+    head, _ = bench.rooflines(dec, {"gemm1_bytes": 1.0, "gemm2_bytes": 1.0},
+                              _phases(gemm1=1.0, gemm2=3.0), _phases(gemm1=5.0, gemm2=2.0))
+    assert head["bound"] == "hbm" and head["kernel"].endswith("true>")
+
+
+def test_host_cpu_model_is_named():
+    assert isinstance(bench.host_cpu_model(), str) and bench.host_cpu_model()
 
 
 def test_traffic_record_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
@@ -125,3 +167,19 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
     assert rec["bytes"] == rec["fetch_bytes"] + rec["write_bytes"]
     assert rec["dispatches"] == [2, 2]
     assert rec["source_sha256"] == P.kernel_source_sha(k)
+
+
+def test_counter_table_ratios(tmp_path):
+    """The counter summary averages each counter per dispatch and rates a
+    kernel's MFMA-busy share against the MFMA probe's own."""
+    k = "k_gemm_dl<true>"
+    _counter_csv(tmp_path / "a", [(1, k, "SQ_VALU_MFMA_BUSY_CYCLES", 40.0),
+                                  (1, k, "SQ_BUSY_CYCLES", 100.0),
+                                  (2, k, "SQ_VALU_MFMA_BUSY_CYCLES", 60.0),
+                                  (2, k, "SQ_BUSY_CYCLES", 100.0),
+                                  (3, "k_mfma_loop", "SQ_VALU_MFMA_BUSY_CYCLES", 90.0),
+                                  (3, "k_mfma_loop", "SQ_BUSY_CYCLES", 100.0)])
+    data = P.counters_by_kernel([str(tmp_path / "a")], [k, "k_mfma_loop"])
+    assert data[k]["SQ_VALU_MFMA_BUSY_CYCLES"] == 50.0 and data[k]["_dispatches"] == 2
+    text = P.counters_table([str(tmp_path / "a")], [k])
+    assert "MFMA busy / SQ busy = 0.5000, 0.556 of the MFMA probe's" in text

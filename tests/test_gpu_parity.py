@@ -93,8 +93,65 @@ def test_small_stagewise(name):
 
 # ------------------------------------------------------------------ full size
 
-@pytest.mark.parametrize("name", I.CONFIG_ORDER)
+ROW_BLOCK = 32  # the shortest M tile of any GEMM path (decode and fp32 tiles)
+
+
+def covering_rows(offsets, n_groups, rng, block=ROW_BLOCK):
+    """Sorted rows to check at full size: for every expert group, its first
+    and last row and one random row in each block of `block` rows counted
+    from the group's start.  Every M tile of the expert GEMMs starts at a
+    group start plus a multiple of 32 rows, so each tile (and with it every
+    (M tile, N tile) item of both GEMMs: a row's output needs all N tiles)
+    holds at least one checked row."""
+    rows = []
+    for e in range(n_groups):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows += [lo, hi - 1]
+        rows += [int(rng.integers(b, min(b + block, hi))) for b in range(lo, hi, block)]
+    return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def covering_tokens(cfg, perm, offsets, rng):
+    """Tokens whose outputs are checked: the tokens of covering_rows, plus,
+    for the shared experts (groups of all tokens in order), the first, the
+    last and one random token in every block of ROW_BLOCK tokens; every
+    token when the layer is small."""
+    if cfg.T <= 64:
+        return np.arange(cfg.T)
+    tok = [0, cfg.T - 1]
+    if cfg.router != I.ROUTER_PRODUCT_KEY and cfg.E_ffn > 0:
+        tok += list(perm[covering_rows(offsets, cfg.E_ffn, rng)] // cfg.k)
+    if cfg.n_shared or cfg.router == I.ROUTER_PRODUCT_KEY:
+        tok += [int(rng.integers(b, min(b + ROW_BLOCK, cfg.T)))
+                for b in range(0, cfg.T, ROW_BLOCK)]
+    return np.unique(np.asarray(tok, dtype=np.int64))
+
+
+def assert_items_covered(cfg, perm, offsets, tokens):
+    """Every ROW_BLOCK-row block of every routed group, and every block of
+    the shared groups, holds a row of a checked token."""
+    chk = np.zeros(cfg.T, dtype=bool)
+    chk[tokens] = True
+    if cfg.router != I.ROUTER_PRODUCT_KEY:
+        row_ok = chk[perm // cfg.k]
+        for e in range(cfg.E_ffn):
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            for b in range(lo, hi, ROW_BLOCK):
+                assert row_ok[b:min(b + ROW_BLOCK, hi)].any(), (e, b)
+    if cfg.n_shared:
+        for b in range(0, cfg.T, ROW_BLOCK):
+            assert chk[b:b + ROW_BLOCK].any(), b
+
+
+@pytest.mark.parametrize("name", I.CONFIG_ORDER + I.EXTRA_ORDER)
 def test_full_size(name):
+    """Full-size layer in the launch configuration the bench times.
+    Routing and dispatch: every token.  Expert stage (moe_expert_ffn):
+    SwiGLU layers on a row in every 32-row block of every group, atomic
+    layers on every task's activation.  Outputs: the tokens of those rows
+    and of every 32-token block of the shared experts' groups."""
     cfg = I.CONFIGS[name]
     say("full size", name, "T", cfg.T)
     inp = full_inputs(name)
@@ -109,17 +166,33 @@ def test_full_size(name):
     say("  routing ok, near-tie tokens:", ties)
     counts, offsets, perm, inv = layer.dispatch(idx)
     torch.cuda.synchronize()
-    C.check_dispatch(cfg, idx_np, counts.cpu().numpy(), offsets.cpu().numpy(),
-                     perm.cpu().numpy(), inv.cpu().numpy())
+    offsets_np, perm_np = offsets.cpu().numpy(), perm.cpu().numpy()
+    C.check_dispatch(cfg, idx_np, counts.cpu().numpy(), offsets_np, perm_np,
+                     inv.cpu().numpy())
+    say("  dispatch ok")
     rng = np.random.default_rng(0)
-    n_s = min(cfg.T, 48)
-    tok = np.sort(rng.choice(cfg.T, size=n_s, replace=False))
-    tok[0], tok[-1] = 0, cfg.T - 1
-    tok = np.unique(tok)
+    y, sy = layer.expert_ffn(x, idx, perm, offsets)
+    torch.cuda.synchronize()
+    tol = C.out_tol(cfg)
+    if cfg.router == I.ROUTER_PRODUCT_KEY:
+        h_ref = O.atomic_h(cfg, inp, idx_np, perm_np)
+        h = y.cpu().numpy()[:h_ref.size]
+        err = np.max(np.abs(h - h_ref)) / max(1.0, np.max(np.abs(h_ref)))
+        say("  every task's activation, max error", err)
+        assert err <= tol
+    else:
+        rows = covering_rows(offsets_np, cfg.E_ffn, rng)
+        sub_off = np.searchsorted(rows, offsets_np[:cfg.E_ffn + 1])
+        Y_ref, _ = O.expert_ffn(cfg.replace(n_shared=0), inp, idx_np, perm_np[rows], sub_off)
+        err = C.max_rel_l2(np_of(y)[rows], Y_ref)
+        say("  expert rows", rows.size, "of", int(offsets_np[cfg.E_ffn]), "rel-L2", err)
+        assert err <= tol
+    tok = covering_tokens(cfg, perm_np, offsets_np, rng)
+    assert_items_covered(cfg, perm_np, offsets_np, tok)
     ref, _, _ = O.forward(cfg, inp, idx_np, gate_np.astype(np.float64), tokens=tok)
     err = C.max_rel_l2(np_of(out)[tok], ref)
-    say("  sampled output rel-L2", err)
-    assert err <= C.out_tol(cfg)
+    say("  output tokens", tok.size, "rel-L2", err)
+    assert err <= tol
 
 
 # ------------------------------------------------------------------ edge cases

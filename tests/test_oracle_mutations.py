@@ -101,6 +101,34 @@ def _combine_no_shared(cfg, inp, idx, gate, inv_perm, Y, SY, tokens=None, _orig=
     return _orig(cfg.replace(n_shared=0), inp, idx, gate, inv_perm, Y, SY, tokens)
 
 
+def _expert_ffn_shared_reversed(cfg, inp, idx, perm, offsets, _orig=O.expert_ffn):
+    """Shared block s computed with shared expert n_shared-1-s."""
+    Y, SY = _orig(cfg, inp, idx, perm, offsets)
+    T = SY.shape[0] // max(cfg.n_shared, 1)
+    blocks = [SY[s * T:(s + 1) * T] for s in range(cfg.n_shared)][::-1]
+    return Y, (np.concatenate(blocks, 0) if blocks else SY)
+
+
+def _expert_ffn_up_from_next_shared(cfg, inp, idx, perm, offsets, _orig=O.expert_ffn):
+    """Shared expert s's up projection taken from expert s+1 (mod n)."""
+    if cfg.n_shared < 2:
+        return _orig(cfg, inp, idx, perm, offsets)
+    inp2 = dict(inp)
+    inp2["shared_up"] = np.roll(inp["shared_up"], -1, axis=0)
+    return _orig(cfg, inp2, idx, perm, offsets)
+
+
+def _expert_ffn_token_index(cfg, inp, idx, perm, offsets, _orig=O.expert_ffn):
+    """Routed rows read token perm[p] % T instead of perm[p] // k."""
+    T = inp["x"].shape[0]
+    x2 = inp["x"][(np.arange(T) * cfg.k) % T] if T else inp["x"]
+    inp2 = dict(inp)
+    inp2["x"] = x2
+    Y, _ = _orig(cfg, inp2, idx, perm, offsets)
+    _, SY = _orig(cfg, inp, idx, perm, offsets)
+    return Y, SY
+
+
 MUTANTS = {
     "router_logits": _no_bias,
     "router_logits#tau": _tau_everywhere,
@@ -115,6 +143,9 @@ MUTANTS = {
     "route_softmax_topk": _no_renorm,
     "softmax": _softmax_no_shift_wrong_axis,
     "combine": _combine_no_shared,
+    "expert_ffn#shared_reversed": _expert_ffn_shared_reversed,
+    "expert_ffn#shared_up_shifted": _expert_ffn_up_from_next_shared,
+    "expert_ffn#token_index": _expert_ffn_token_index,
 }
 
 

@@ -475,3 +475,31 @@ def test_shared_experts_weight_one_and_sum():
             routed[t] += gate[t, j] * _torch_swiglu(X[t:t + 1], f64(inp["w_gate"][e]),
                                                     f64(inp["w_up"][e]), f64(inp["w_down"][e]))[0]
     assert np.allclose(out, shared + routed, rtol=1e-11, atol=1e-12)
+
+
+def test_expert_ffn_rows_and_shared_blocks():
+    """expert_ffn's own outputs, row by row, against torch SwiGLUs: routed
+    row p is expert idx[task] on token task // k for task perm[p]; shared
+    block s (rows s*T .. s*T+T-1) is shared expert s on every token, in
+    token order.  Three shared experts, so a swapped or reversed shared
+    index, or one expert's weights used for another, fails."""
+    cfg = I.small_variant("deepseek16b").replace(T=21, n_shared=3, f_shared=128)
+    inp = I.make_inputs(cfg)
+    idx, _, _ = O.route(cfg, inp)
+    counts, offsets, perm, inv = O.dispatch(idx, cfg.E)
+    Y, SY = O.expert_ffn(cfg, inp, idx, perm, offsets)
+    X = f64(inp["x"])
+    assert Y.shape == (cfg.T * cfg.k, cfg.d) and SY.shape == (cfg.n_shared * cfg.T, cfg.d)
+    for p in range(Y.shape[0]):
+        task = int(perm[p])
+        t, e = task // cfg.k, int(idx.reshape(-1)[task])
+        ref = _torch_swiglu(X[t:t + 1], f64(inp["w_gate"][e]), f64(inp["w_up"][e]),
+                            f64(inp["w_down"][e]))[0]
+        assert np.allclose(Y[p], ref, rtol=1e-12, atol=1e-13), p
+    for s in range(cfg.n_shared):
+        ref = _torch_swiglu(X, f64(inp["shared_gate"][s]), f64(inp["shared_up"][s]),
+                            f64(inp["shared_down"][s]))
+        assert np.allclose(SY[s * cfg.T:(s + 1) * cfg.T], ref, rtol=1e-12, atol=1e-13), s
+    # the experts differ, so the blocks must too (a pin that cannot tell
+    # shared expert 0 from 1 would pin nothing)
+    assert not np.allclose(SY[:cfg.T], SY[cfg.T:2 * cfg.T])
