@@ -60,6 +60,8 @@ extern "C" {
 #define MOE_ERR_WORKSPACE   4  /* ws_bytes smaller than moe_workspace_size    */
 #define MOE_ERR_UNSUPPORTED 5  /* valid request this build does not implement */
 #define MOE_ERR_HIP         6  /* a HIP launch reported an error              */
+#define MOE_ERR_SCRATCH     7  /* moe_forward_noalloc: the pass needs more than
+                                  MOE_NOALLOC_SCRATCH_BYTES of workspace     */
 
 /* layer dtypes */
 #define MOE_F32  0
@@ -253,6 +255,30 @@ int32_t moe_forward_traced(const moe_dims* dims, const moe_weights* w,
                            int32_t* topk_idx_opt, float* topk_gate_opt,
                            void* ws, size_t ws_bytes, moe_stream stream,
                            void* const* events);
+
+/* Static workspace of moe_forward_noalloc, per GPU: 64 MiB. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * file-scope device array of MOE_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends; its device address is looked
+ * up once per device, on the first call with that device current.  The
+ * caller still passes x, out and the optional routing outputs; stream must
+ * belong to the current device.
+ *   Limit: a call whose moe_workspace_size(dims, T) exceeds
+ *   MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH before any GPU call
+ *   (about 2,000 tokens of the MoE++-shaped layer, 1,200 of the
+ *   DeepSeek-shaped one; a 16-token decode batch needs under 1 MiB).
+ *   Concurrency: all calls on one GPU share its array, which keeps the last
+ *   call's contents; calls that overlap on one GPU (other streams, other
+ *   threads) race and must be serialised by the caller.
+ * Arguments, results and other errors as moe_forward.  It calls no hipMalloc,
+ * hipFree or other allocating routine. */
+int32_t moe_forward_noalloc(const moe_dims* dims, const moe_weights* w, const void* x,
+                            int64_t T, void* out, int32_t* topk_idx_opt,
+                            float* topk_gate_opt, moe_stream stream);
 
 #ifdef __cplusplus
 }

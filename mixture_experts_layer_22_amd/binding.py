@@ -22,13 +22,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, 1, 2, 3
-MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 4, 5, 6
+MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_SCRATCH = 4, 5, 6, 7
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_F32, MOE_BF16 = 0, 1
 MOE_MAX_ZC = 8
 
 EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route", "moe_router_logits",
             "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-            "moe_forward_traced"]
+            "moe_forward_traced", "moe_forward_noalloc"]
 MOE_N_PHASES = 7
 PHASES = ["route", "dispatch", "tiles", "atomic", "gemm1", "gemm2", "combine"]
 
@@ -93,6 +94,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_combine.argtypes = [dims_p, w_p, P, i64, P, P, P, P, P, P, P]
     lib.moe_forward.restype = ctypes.c_int32
     lib.moe_forward.argtypes = [dims_p, w_p, P, i64, P, P, P, P, sz, P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int32
+    lib.moe_forward_noalloc.argtypes = [dims_p, w_p, P, i64, P, P, P, P]
     lib.moe_forward_traced.restype = ctypes.c_int32
     lib.moe_forward_traced.argtypes = [dims_p, w_p, P, i64, P, P, P, P, sz, P,
                                        ctypes.POINTER(ctypes.c_void_p)]
@@ -220,6 +223,14 @@ def moe_forward(dims, w: DeviceWeights, x, T, out, ws, topk_idx=None, topk_gate=
     _check(load().moe_forward(ctypes.byref(dims), ctypes.byref(w.struct), _ptr(x), int(T),
                               _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(ws),
                               0 if ws is None else ws.numel(), _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(dims, w: DeviceWeights, x, T, out, topk_idx=None, topk_gate=None,
+                        stream=None):
+    """moe_forward on the library's static per-GPU scratch (no workspace)."""
+    _check(load().moe_forward_noalloc(ctypes.byref(dims), ctypes.byref(w.struct), _ptr(x),
+                                      int(T), _ptr(out), _ptr(topk_idx), _ptr(topk_gate),
+                                      _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_forward_traced(dims, w: DeviceWeights, x, T, out, ws, events, topk_idx=None,

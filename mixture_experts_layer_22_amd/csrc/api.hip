@@ -4,6 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kernels.h"
 
 using namespace moe;
@@ -323,6 +326,7 @@ const char* moe_status_str(int32_t s) {
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_UNSUPPORTED: return "unsupported request";
     case MOE_ERR_HIP: return "HIP error";
+    case MOE_ERR_SCRATCH: return "request exceeds the static scratch of moe_forward_noalloc";
     default: return "unknown status";
   }
 }
@@ -476,3 +480,59 @@ int32_t moe_forward(const moe_dims* dims, const moe_weights* w, const void* x, i
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- static scratch
+
+namespace {
+
+// The workspace of moe_forward_noalloc: one array in device memory, which
+// the loader places on every GPU the library runs on and which stays there
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in); it uses the device address
+// that hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, looked up on the first
+// call on that device (with it current) and kept.
+int32_t scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t moe_forward_noalloc(const moe_dims* dims, const moe_weights* w,
+                                       const void* x, int64_t T, void* out,
+                                       int32_t* topk_idx_opt, float* topk_gate_opt,
+                                       moe_stream stream) {
+  // the same validation as moe_forward, then the size limit, all before
+  // any HIP call
+  int32_t s = validate_dims(dims, T);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(dims, w, true, true, true)) != MOE_OK) return s;
+  if (T > 0 && (!x || !out)) return MOE_ERR_NULL;
+  if (misaligned(x) || misaligned(out)) return MOE_ERR_SHAPE;
+  if (make_layout(dims, T).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  if (T == 0) return MOE_OK;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != MOE_OK) return s;
+  // every region the pass reads is written earlier in the same pass (the
+  // dispatch zeroes its own counters), so nothing needs clearing
+  return moe_forward_traced(dims, w, x, T, out, topk_idx_opt, topk_gate_opt, ws,
+                            (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert isinstance(B.status_str(s), str) and B.status_str(s)
     assert B.status_str(99) == "unknown status"
 
@@ -273,3 +273,28 @@ def test_probes_reject_on_host(prb):
     assert mfma(0, P, 4, None) == B.MOE_ERR_SHAPE
     assert mfma((1 << 19) + 1, P, 4, None) == B.MOE_ERR_SHAPE
     assert mfma(10, P, 0, None) == B.MOE_ERR_SHAPE
+
+
+def test_noalloc_rejects_on_host(lib):
+    """moe_forward_noalloc validates like moe_forward and refuses, before any
+    GPU call, a pass whose workspace exceeds its static scratch."""
+    cfg = I.CONFIGS["moepp"]
+    dims = B.dims_from_config(cfg)
+    w = B.MoeWeights()
+    for n in ["router_w", "w_gate", "w_up", "w_down", "const_wc", "const_v"]:
+        setattr(w, n, FAKE)
+    f = lib.moe_forward_noalloc
+    big = 1 << 16
+    assert B.moe_workspace_size(dims, big) > B.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(dims), ctypes.byref(w), FAKE, big, FAKE, None, None, None) == \
+        B.MOE_ERR_SCRATCH
+    assert f(ctypes.byref(dims), ctypes.byref(w), None, 16, FAKE, None, None, None) == \
+        B.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), None, FAKE, 16, FAKE, None, None, None) == B.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), ctypes.byref(w), FAKE + 4, 16, FAKE, None, None, None) == \
+        B.MOE_ERR_SHAPE
+    assert f(ctypes.byref(dims), ctypes.byref(w), FAKE, 0, FAKE, None, None, None) == B.MOE_OK
+    bad = _dims(k=0)
+    assert f(ctypes.byref(bad), ctypes.byref(w), FAKE, 16, FAKE, None, None, None) == \
+        B.MOE_ERR_SHAPE
+    assert "static scratch" in B.status_str(B.MOE_ERR_SCRATCH)
