@@ -541,6 +541,202 @@ __device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx
   gemm_epilogue<BMT, SWIGLU, FM, FN>(args, c, n0, lds, acc, wm, wn);
 }
 
+// vmcnt(n) for a wave-uniform n in [0, 20]
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 19: wait_vmcnt<19>(); break;
+    default: wait_vmcnt<20>(); break;
+  }
+}
+
+// The tile's K loop with 64-wide K tiles: every LDS row holds 128 bytes of
+// K, so each copy instruction moves 8 whole 128-byte rows (full cache lines)
+// rather than 16 half lines.  The LDS is a ring of 20 slots of 64 rows
+// (8 KB); K tile t takes S = BMT/64 + 4 consecutive slots of the ring (its
+// A rows, then its B rows), so 20/S tiles are resident or in flight: 2.5 at
+// 256 rows, 4 at 64 rows.  One slot is one copy instruction per wave (wave w
+// moves rows 8w .. 8w+7 of it).  Copies are numbered in ring order; tile t's
+// are numbers [tS, (t+1)S).  A K tile is two K steps of 32 (one MFMA each);
+// the barrier comes once per K tile, in its second step: it publishes tile
+// t+1 and frees tile t's slots, which then take copies 20 + tS ..
+// 20 + (t+1)S - 1, issued over that step's MFMA rows.  16-byte chunk c of
+// row r sits at c ^ ((r >> 1) & 7): a fragment read (16 rows, one chunk
+// each) and a copy (8 rows x 8 chunks) touch every bank once per 16 lanes.
+template <int BMT, bool SWIGLU>
+__device__ __forceinline__ void gemm_tile_ring(const GemmArgs& args, const TileCtx<SWIGLU>& c,
+                                               int n0, uint16_t* lds) {
+  constexpr int BN = 256, BK = 64, SROWS = 64;
+  constexpr int SLOT = SROWS * BK;           // elements per slot (8 KB)
+  constexpr int NSLOT = kGemmLdsElems / SLOT;
+  constexpr int SA = BMT / SROWS, SB = BN / SROWS;
+  constexpr int S = SA + SB;                 // slots per K tile
+  constexpr int AHEAD = NSLOT - 2 * S;       // copies still in flight at a steady barrier
+  constexpr int NW = kGemmThreads / 64;
+  constexpr int FM = BMT / 32, FN = 4;
+  constexpr int CPR = (S + FM - 1) / FM;     // copies per MFMA row after the barrier
+  static_assert(NSLOT == 20 && BMT % SROWS == 0 && AHEAD >= 0 && NW * 8 == SROWS, "ring");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  auto swz = [](int r) { return (r >> 1) & 7; };
+
+  // source of this wave's copy of slot j of a tile (rows 8 wave .. +7 of
+  // the slot); the lane's 16 bytes are logical chunk (lane & 7) ^ swz(row)
+  // of its row's 128-byte K slice.  Rows past the group's end or past N
+  // point at a valid row.
+  const uint16_t* src[S];
+#pragma unroll
+  for (int j = 0; j < S; j++) {
+    const int rr = 8 * wave + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(rr);
+    const uint16_t* p;
+    if (j < SA) {
+      p = a_row<uint16_t, SWIGLU>(args, c, j * SROWS + rr);
+      if (!p) p = a_row<uint16_t, SWIGLU>(args, c, 0);
+    } else {
+      const int r = (j - SA) * SROWS + rr;
+      p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, r);
+      if (!p) p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, SWIGLU && r >= BN / 2 ? BN / 2 : 0);
+    }
+    src[j] = p + chunk * 8;
+  }
+  // shared group of the down projection: K slices in separate blocks (the
+  // delta is 0 elsewhere)
+  const int64_t seg_step = c.shared ? args.b_seg_shared - args.k_seg_shared : 0;
+  const int seg_tiles = c.shared ? args.k_seg_shared / BK : 1;
+  const int nk = c.K / BK;
+  // copy number q (tile q / S, slot q % S) into ring slot q % NSLOT
+  auto copy_q = [&](int tq, int j, int pos) {
+    const int64_t bdel = (j >= SA && seg_step) ? (int64_t)(tq / seg_tiles) * seg_step : 0;
+    dl_copy16(src[j] + tq * BK + bdel, lds + pos * SLOT + 8 * wave * BK);
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++) acc[i][j] = f32x4{};
+
+  int brow[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; fn++)
+    brow[fn] = SWIGLU ? (fn < 2 ? wn * 32 + fn * 16 : BN / 2 + wn * 32 + (fn - 2) * 16)
+                      : wn * 64 + fn * 16;
+  const int frow = lane & 15;
+  const int fch0 = ((lane >> 4) ^ swz(frow)) * 8;        // K step 0 of a tile
+  const int fch1 = ((4 + (lane >> 4)) ^ swz(frow)) * 8;  // K step 1
+
+  bf16x8 afr[FM];
+  bf16x8 bfr[FN];
+  auto ring = [](int p) { return p >= NSLOT ? p - NSLOT : p; };
+  // pt: ring slot of tile t's slot 0
+  auto read_a = [&](int pt, int fch, int fm) {
+    const int row = wm * (BMT / 2) + fm * 16;  // wave-uniform; + frow
+    const int pos = ring(pt + row / SROWS);
+    afr[fm] = *reinterpret_cast<const bf16x8*>(lds + pos * SLOT + (row % SROWS + frow) * BK + fch);
+  };
+  auto read_b = [&](int pt, int fch, int fn) {
+    const int pos = ring(pt + SA + brow[fn] / SROWS);
+    bfr[fn] = *reinterpret_cast<const bf16x8*>(lds + pos * SLOT +
+                                               (brow[fn] % SROWS + frow) * BK + fch);
+  };
+  auto mfma_row = [&](int fm) {
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], afr[fm], acc[fm][fn], 0, 0, 0);
+  };
+
+  // One K step: row 0 multiplies first; in a tile's second step the barrier
+  // follows (this wave's copies of tile t+1 landed, its reads of tile t
+  // done, then everyone's).  Rows 1.. issue the copy batch the barrier
+  // allowed (tile t's copies t*S .. , qbase = 20 + t*S, into ring slots
+  // from pfree) and read the next step's fragments (ring slot np of its
+  // tile, chunk offset nfch).
+  auto kstep = [&](bool bar, bool more, bool copy, int t, int np, int nfch, int pfree,
+                   int wait_n) {
+    mfma_row(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (bar) {
+      wait_vmcnt_n(wait_n);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads are done
+      __builtin_amdgcn_s_barrier();
+    }
+#pragma unroll
+    for (int fm = 1; fm <= FM; fm++) {
+      if (fm < FM) mfma_row(fm);
+      if (copy) {
+#pragma unroll
+        for (int i = (fm - 1) * CPR; i < fm * CPR && i < S; i++) {
+          const int tq = t + (NSLOT + i) / S;  // copy 20 + t*S + i
+          if (tq < nk) copy_q(tq, (NSLOT + i) % S, ring(pfree + i));
+        }
+      }
+      if (more) {
+        if (fm == 1) read_a(np, nfch, 0);
+        if (fm < FM) read_a(np, nfch, fm);
+        if (fm == FM)
+#pragma unroll
+          for (int fn = 0; fn < FN; fn++) read_b(np, nfch, fn);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // prologue: copies 0 .. min(20, nk S) - 1 (slots in ring order), tile 0
+  // published, its first step's fragments in registers
+  const int pro = nk * S < NSLOT ? nk * S : NSLOT;
+#pragma unroll
+  for (int q = 0; q < NSLOT; q++)
+    if (q < pro) copy_q(q / S, q % S, q);
+  wait_vmcnt_n(pro - S);
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int fm = 0; fm < FM; fm++) read_a(0, fch0, fm);
+#pragma unroll
+  for (int fn = 0; fn < FN; fn++) read_b(0, fch0, fn);
+
+  int t = 0, pt = 0;  // pt: ring slot of tile t's first slot
+  // steady state: every copy of the batch exists (20 + (t+1) S <= nk S)
+  for (; NSLOT + (t + 1) * S <= nk * S; t++) {
+    const int pn = ring(pt + S);
+    kstep(false, true, false, t, pt, fch1, 0, 0);
+    kstep(true, true, true, t, pn, fch0, pt, AHEAD);
+    pt = pn;
+  }
+  // drain: copies past the last tile are skipped
+  for (; t < nk; t++) {
+    const int pn = ring(pt + S);
+    kstep(false, true, false, t, pt, fch1, 0, 0);
+    const bool last = t + 1 >= nk;
+    // copies issued before this barrier: min(20 + t S, nk S); needed: (t+2) S
+    const int issued = NSLOT + t * S < nk * S ? NSLOT + t * S : nk * S;
+    kstep(!last, !last, !last, t, pn, fch0, pt, issued - (t + 2) * S);
+    pt = pn;
+  }
+
+  gemm_epilogue<BMT, SWIGLU, FM, FN>(args, c, n0, lds, acc, wm, wn);
+}
+
 // A tile runs the variant of 64, 128, 192 or 256 rows that covers its valid
 // rows, so the last tile of a group (and the small groups of the long tail
 // of expert loads) wastes at most 63 rows of MFMA work.
@@ -572,13 +768,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dl(GemmArgs args) {
   const int n0 = n_tile * (SWIGLU ? 128 : 256);
   if (n0 >= c.N) return;
   if (c.nr > 192)
-    gemm_tile_dl<256, SWIGLU>(args, c, n0, lds);
+    gemm_tile_ring<256, SWIGLU>(args, c, n0, lds);
   else if (c.nr > 128)
-    gemm_tile_dl<192, SWIGLU>(args, c, n0, lds);
+    gemm_tile_ring<192, SWIGLU>(args, c, n0, lds);
   else if (c.nr > 64)
-    gemm_tile_dl<128, SWIGLU>(args, c, n0, lds);
+    gemm_tile_ring<128, SWIGLU>(args, c, n0, lds);
   else
-    gemm_tile_dl<64, SWIGLU>(args, c, n0, lds);
+    gemm_tile_ring<64, SWIGLU>(args, c, n0, lds);
 }
 
 // ------------------------------------------------------------------------
