@@ -69,6 +69,8 @@ def algorithmic_work(cfg, counts):
             # per task its expert id, gate, sorted position and activation
             "atomic_combine_bytes": (touched + T * (2 if cfg.n_shared else 1)) * d * es
                                     + n * 16,
+            # what the combine's row loads request: every task's out-vector
+            "atomic_gather_bytes": n * d * es,
             "gemm1_flop": 4.0 * d * rows_s,
             "gemm2_flop": 2.0 * d * rows_s,
         }
@@ -443,6 +445,16 @@ def main():
     read_gbs = n_rd * 4 / (best_ms(lambda: B.moe_probe_stream_read(
         rd_buf, n_rd, rd_sums, rd_blocks, stream)) * 1e-3) / 1e9
     del rd_buf, rd_sums
+    gather_gbs = None
+    if cfg.router == I.ROUTER_PRODUCT_KEY:
+        # the atomic combine's reads alone: every token's k rows of the W
+        # table, this step's routing, nothing else done with them
+        aw = layer.weights.tensors["atom_w"]
+        g_sums = torch.empty(T, dtype=torch.float32, device=dev)
+        row_bytes = cfg.d * aw.element_size()
+        gather_gbs = T * cfg.k * row_bytes / (best_ms(lambda: B.moe_probe_row_gather(
+            aw, cfg.E, row_bytes, idx, T * cfg.k, cfg.k, g_sums, stream)) * 1e-3) / 1e9
+        del g_sums
     mf_iters, mf_blocks = 4096, 512
     mf_out = torch.empty(mf_blocks, dtype=torch.float32, device=dev)
     mf_flop = 2.0 * 16 * 16 * 32 * 16 * 8 * mf_iters * mf_blocks
@@ -458,6 +470,13 @@ def main():
     ceiling = {"hbm_read_gbs": read_gbs, "mfma_bf16_tflops": mfma_tflops,
                "frac_of_measured": roof["achieved"] / (read_gbs if roof["unit"] == "GB/s"
                                                        else mfma_tflops)}
+    if gather_gbs is not None:
+        # the combine's requested bytes (T k rows) against the same rows
+        # gathered by the probe
+        comb = [r for r in stages if r["phase"] == "combine"][0]
+        ceiling["row_gather_gbs"] = gather_gbs
+        ceiling["combine_requested_gbs"] = work["atomic_gather_bytes"] / (comb["us"] * 1e-6) / 1e9
+        ceiling["combine_frac_of_gather"] = ceiling["combine_requested_gbs"] / gather_gbs
     expert_flop = work["expert1_flop"] + work["expert2_flop"]
     line = {
         "metric": METRIC,

@@ -40,7 +40,10 @@
  *
  * Task numbering: task tau = t*k + j is token t's j-th choice (j ordered by
  * descending router score).  perm[p] is the task at sorted position p;
- * sorted order is (expert id, token id) ascending; inv_perm[perm[p]] = p.
+ * sorted order is (group, task id) ascending, a group being a contiguous
+ * range of expert ids: one expert for softmax top-k routers, one row of the
+ * expert grid (pk_cols ids, group = id / pk_cols) for product-key routers;
+ * inv_perm[perm[p]] = p.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -184,10 +187,14 @@ int32_t moe_router_logits(const moe_dims* dims, const moe_weights* w, const void
                           moe_stream stream);
 
 /* Expert-centric dispatch (OmniMoE page sec. 2.2, Task Collection and
- * Grouping & Sorting): a stable sort of the T*k tasks by expert id.
+ * Grouping & Sorting: tasks grouped by contiguous ranges of expert ids,
+ * sorted by token inside a group): a stable sort of the T*k task ids by
+ * group.  G groups: G = E for softmax top-k routers (one expert each), G =
+ * pk_rows for product-key routers (one row of the expert grid each).
  *   topk_idx  int32 [T, k] in; every id in [0, E).
- *   counts    out: int32 [E] tasks per expert.
- *   offsets   out: int32 [E+1] exclusive prefix sum of counts.
+ *   counts    out: int32 [E] buffer; entries 0..G-1 = tasks per group.
+ *   offsets   out: int32 [E+1] buffer; entries 0..G = exclusive prefix sum
+ *             of counts (offsets[G] = T*k).  Later entries are not written.
  *   perm      out: int32 [T*k] task id at each sorted position.
  *   inv_perm  out: int32 [T*k] sorted position of each task.
  * Zero-computation experts have the highest ids: their tasks form the tail

@@ -24,6 +24,23 @@ extern "C" {
 int32_t moe_probe_stream_read(const float* buf, int64_t n, float* block_sums, int blocks,
                               moe_stream stream);
 
+/* Row gather: n_idx / per_wave waves; wave w reads the table rows
+ * idx[w*per_wave .. (w+1)*per_wave) whole (row_bytes each, 16-byte loads,
+ * 8 rows in flight) and sums them as fp32: the access pattern of a token
+ * gathering its k atomic experts' rows, with no other work.  n_idx *
+ * row_bytes bytes are requested.
+ *
+ * table: device, n_rows * row_bytes bytes, 16-byte aligned; row_bytes in
+ *   {1024, 2048, 4096, 8192}.  idx: device int32 [n_idx]; entries outside
+ *   [0, n_rows) are clamped.  per_wave in [1, 64], n_idx % per_wave == 0.
+ * wave_sums: device, n_idx / per_wave floats, written.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE; nothing is written on error.
+ *   Asynchronous on `stream`; allocates nothing.
+ */
+int32_t moe_probe_row_gather(const void* table, int64_t n_rows, int row_bytes,
+                             const int32_t* idx, int64_t n_idx, int per_wave,
+                             float* wave_sums, moe_stream stream);
+
 /* MFMA loop: `blocks` blocks of 8 waves, each wave issuing `iters` rounds of
  * 16 independent v_mfma_f32_16x16x32_bf16 on all-ones operands, with no
  * memory traffic: 2*16*16*32 * 16 * 8 * iters * blocks FLOP.  Every

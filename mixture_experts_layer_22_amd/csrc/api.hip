@@ -62,6 +62,12 @@ int n_const_of(const moe_dims* d) {
   return c;
 }
 
+// Dispatch groups: contiguous ranges of expert ids whose tasks are sorted
+// together (OmniMoE page sec. 2.2, Grouping & Sorting): one expert each for
+// FFN experts, one row of the expert grid for atomic experts.
+int dispatch_width(const moe_dims* d) { return is_pk(d) ? d->pk_cols : 1; }
+int dispatch_groups(const moe_dims* d) { return (int)cdiv(d->E, dispatch_width(d)); }
+
 bool misaligned(const void* p) { return p && ((uintptr_t)p % 16) != 0; }
 
 // Workspace layout (one figure for every entry point).
@@ -96,7 +102,7 @@ Layout make_layout(const moe_dims* d, int64_t T) {
     return o;
   };
   L.logits = take((size_t)L.splits * T * L.NL * 4);
-  L.disp = take((size_t)dispatch_scratch_ints(L.n, d->E) * 4);
+  L.disp = take((size_t)dispatch_scratch_ints(L.n, dispatch_groups(d)) * 4);
   L.tiles = take((size_t)L.max_tiles * sizeof(int4));
   L.ntiles = take(kSchedInts * 4);
   L.h = take(is_pk(d) ? 0 : (size_t)L.n * d->f * es);
@@ -392,7 +398,8 @@ int32_t moe_dispatch(const moe_dims* dims, const int32_t* topk_idx, int64_t T, i
   Layout L = make_layout(dims, T);
   if ((s = check_ws(L, ws, ws_bytes)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
-  MOE_TRY(launch_dispatch(topk_idx, L.n, dims->E, counts, offsets, perm, inv_perm,
+  MOE_TRY(launch_dispatch(topk_idx, L.n, dims->E, dispatch_width(dims), counts, offsets, perm,
+                          inv_perm,
                           at<int32_t*>(ws, L.disp), (hipStream_t)stream));
   return MOE_OK;
 }
@@ -459,8 +466,8 @@ int32_t moe_forward_traced(const moe_dims* dims, const moe_weights* w, const voi
   MOE_TRY(mark(1));
   // a single-pass dispatch also builds the expert GEMMs' tile list
   const TileBuild tb = tile_build(dims, T, ws, L);
-  const bool fused = tb.tiles && dispatch_builds_tiles(L.n, dims->E);
-  MOE_TRY(launch_dispatch(idx, L.n, dims->E, counts, offsets, perm, inv,
+  const bool fused = tb.tiles && dispatch_builds_tiles(L.n, dispatch_groups(dims));
+  MOE_TRY(launch_dispatch(idx, L.n, dims->E, dispatch_width(dims), counts, offsets, perm, inv,
                           at<int32_t*>(ws, L.disp), st, fused ? &tb : nullptr));
   MOE_TRY(mark(2));
   if ((s = do_experts(dims, w, x, T, idx, perm, offsets, y, sy, ws, L, st, events, fused)) !=

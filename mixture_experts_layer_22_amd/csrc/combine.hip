@@ -39,6 +39,30 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
 };
 
+// s + a . b over 8 elements: bf16 pairs through v_dot2_f32_bf16 (both
+// products exact, fp32 sums), fp32 through 8 FMAs in element order.  The
+// pairs are taken from the whole 8-element vector with shufflevector: a bit
+// cast of one 32-bit element of the packed vector to a bf16 pair is
+// compiled as element 0 every time by this compiler.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8(const Raw8<uint16_t>& a, const Raw8<uint16_t>& b, float s) {
+  const bf16x8 x = __builtin_bit_cast(bf16x8, a.w), y = __builtin_bit_cast(bf16x8, b.w);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1),
+                                      __builtin_shufflevector(y, y, 0, 1), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3),
+                                      __builtin_shufflevector(y, y, 2, 3), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5),
+                                      __builtin_shufflevector(y, y, 4, 5), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7),
+                                      __builtin_shufflevector(y, y, 6, 7), s, false);
+  return s;
+}
+__device__ __forceinline__ float dot8(const Raw8<float>& a, const Raw8<float>& b, float s) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) s = fmaf(a[i], b[i], s);
+  return s;
+}
+
 __device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
@@ -185,9 +209,17 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 // t*k + j, e = idx[task]).  A wave takes 8 consecutive sorted tasks, 8
 // lanes per task; lane s of a group loads units s, s+8, ... of both rows, so
 // each load instruction reads 8 rows x 128 contiguous bytes and a lane has
-// many loads in flight.  Consecutive tasks of one expert re-read its row
-// from cache, so the table itself streams from HBM about once.
+// many loads in flight.
+//
+// The sorted order groups tasks by row of the expert grid and runs tokens
+// in order inside a row, and each XCD walks one contiguous stretch of it:
+// block b (on XCD b % 8) takes chunk i = b / 8 of XCD b % 8's stretch.  The
+// blocks an XCD runs at once thus cover a few consecutive rows, whose u
+// vectors (pk_cols of them) and tokens' x rows are read from HBM or the
+// memory-side cache once and re-read from the XCD's L2; a token's several
+// tasks in one row are adjacent and share their x row in one load.
 constexpr int kAtomTasksPerWave = 8;
+constexpr int kAtomTasksPerBlock = 4 * kAtomTasksPerWave;
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_atomic_h(const T* __restrict__ x,
@@ -196,7 +228,13 @@ __global__ __launch_bounds__(256) void k_atomic_h(const T* __restrict__ x,
                                                  const int32_t* __restrict__ perm, int64_t n,
                                                  int k, int d, float* __restrict__ h) {
   const int lane = threadIdx.x & 63, sub = lane & 7;
-  const int64_t p = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kAtomTasksPerWave + (lane >> 3);
+  // chunk of this block: XCD x owns chunks [x q + min(x, r), ..) of the
+  // 8 q + r chunks (one more for the first r XCDs)
+  const int64_t nblk = gridDim.x, q = nblk / kXcds, r = nblk % kXcds;
+  const int64_t xcd = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
+  const int64_t chunk = xcd * q + (xcd < r ? xcd : r) + i;
+  const int64_t p = chunk * kAtomTasksPerBlock + (threadIdx.x >> 6) * kAtomTasksPerWave +
+                    (lane >> 3);
   const bool ok = p < n;
   const int32_t task = perm[ok ? p : n - 1];
   const int e = idx[task];
@@ -209,8 +247,7 @@ __global__ __launch_bounds__(256) void k_atomic_h(const T* __restrict__ x,
     Raw8<T> xv, uv;
     xv.load(xr + u * 8);
     uv.load(ur + u * 8);
-#pragma unroll
-    for (int q = 0; q < 8; q++) s = fmaf(uv[q], xv[q], s);
+    s = dot8(uv, xv, s);
   }
   s += __shfl_xor(s, 1, 64);
   s += __shfl_xor(s, 2, 64);
@@ -318,7 +355,7 @@ template <typename T>
 static hipError_t atomic_h_t(const void* x, const void* u, const int32_t* idx,
                              const int32_t* perm, int64_t n, int k, int d, float* h,
                              hipStream_t st) {
-  dim3 grid((unsigned)cdiv(cdiv(n, kAtomTasksPerWave), 4)), block(256);
+  dim3 grid((unsigned)cdiv(n, kAtomTasksPerBlock)), block(256);
   hipLaunchKernelGGL((k_atomic_h<T>), grid, block, 0, st, (const T*)x, (const T*)u, idx, perm, n,
                      k, d, h);
   return hipGetLastError();

@@ -4,8 +4,11 @@
 // Technical Summary sec. 2.2, Expert-Centric Scheduling, steps Task
 // Collection and Grouping & Sorting).
 //
-// The grouping is a stable LSD radix sort of the task ids keyed by expert
-// id, 8 key bits per pass (one pass for up to 256 experts, two for 65,536).
+// A group is a contiguous range of `width` expert ids (one expert for
+// routed FFN experts; one row of the expert grid for atomic experts), so
+// the key of a task is its expert id / width.  The grouping is a stable LSD
+// radix sort of the task ids by that key, 8 key bits per pass (one pass for
+// up to 256 groups).
 // Each pass is a per-tile digit histogram, one exclusive scan over
 // (digit, tile) in digit-major order, and a stable scatter whose in-tile
 // ranks come from wave ballots.  Stability of every pass keeps tasks of one
@@ -70,45 +73,18 @@ __global__ __launch_bounds__(256) void k_digit_scan(int32_t* __restrict__ hist, 
   if (threadIdx.x == 0) totals[blockIdx.x] = carry;
 }
 
-// Single-pass dispatch (E <= 256): exclusive scan of the digit-major tile
-// histogram in place, and from it the expert offsets (the scanned value at
-// (e, tile 0)) and counts.
-__global__ __launch_bounds__(1024) void k_dispatch_scan(int32_t* hist, int64_t len, int nb, int E,
-                                                        int64_t n, int32_t* __restrict__ counts,
-                                                        int32_t* __restrict__ offsets) {
-  __shared__ int32_t wtot[16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t per = (len + 1023) / 1024;
-  const int64_t lo = tid * per;
-  const int64_t hi = lo + per < len ? lo + per : len;
-  int32_t s = 0;
-  for (int64_t i = lo; i < hi; i++) s += hist[i];
-  // exclusive scan of the 1024 thread sums: inside each wave by shuffles,
-  // then across the 16 wave totals
-  int32_t x = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wtot[w] = x;
-  __syncthreads();
-  int32_t run = x - s;
-#pragma unroll
-  for (int ww = 0; ww < 16; ww++) run += ww < w ? wtot[ww] : 0;
-  for (int64_t i = lo; i < hi; i++) {
-    int32_t v = hist[i];
-    hist[i] = run;
-    if (i % nb == 0 && i / nb < E) offsets[i / nb] = run;
-    run += v;
-  }
-  if (tid == 0) offsets[E] = (int32_t)n;
-  __syncthreads();
-  for (int e = tid; e < E; e += 1024) counts[e] = offsets[e + 1] - offsets[e];
+// Group key of an expert id: id / width (a shift when width is a power of
+// two: wshift >= 0).
+struct GroupKey {
+  int width, wshift;
+};
+__device__ __forceinline__ int32_t group_of(int32_t e, GroupKey g) {
+  return g.wshift >= 0 ? (e >> g.wshift) : (int32_t)((uint32_t)e / (uint32_t)g.width);
 }
 
-__device__ __forceinline__ int radix_digit(const int32_t* idx, int32_t task, int shift, int mask) {
-  return (idx[task] >> shift) & mask;
+__device__ __forceinline__ int radix_digit(const int32_t* idx, int32_t task, int shift, int mask,
+                                           GroupKey g) {
+  return (group_of(idx[task], g) >> shift) & mask;
 }
 
 // Per-tile digit histogram: hist[digit * nb + tile].  Also sets zero[0..nz)
@@ -119,7 +95,7 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __r
                                                               int64_t n, int shift, int bits,
                                                               int32_t* __restrict__ hist, int nb,
                                                               int32_t* __restrict__ zero,
-                                                              int64_t nz) {
+                                                              int64_t nz, GroupKey gk) {
   __shared__ int32_t cnt[256];
   const int tid = threadIdx.x;
   for (int64_t i = (int64_t)blockIdx.x * kRadixThreads + tid; i < nz;
@@ -134,7 +110,7 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __r
     int64_t i = base + r * kRadixThreads + tid;
     if (i < n) {
       int32_t task = src ? src[i] : (int32_t)i;
-      atomicAdd(&cnt[radix_digit(idx, task, shift, mask)], 1);
+      atomicAdd(&cnt[radix_digit(idx, task, shift, mask, gk)], 1);
     }
   }
   __syncthreads();
@@ -144,20 +120,19 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const int32_t* __r
 // Stable scatter.  Items of a tile are taken in task order r*256 + w*64 + l;
 // an item's destination is base[digit, tile] + (same-digit items earlier in
 // the tile).  Same-digit lanes of a wave are found with one ballot per key
-// bit.  base[digit, tile] is the scanned histogram, plus the exclusive scan
-// of the digit totals when those are given (multi-pass sorts); or, with
-// scan_self (single pass, few tiles), each block scans the raw histogram
-// itself: its digit's earlier tiles plus all smaller digits.  The last pass
-// also writes the inverse permutation.  Block nb, when launched, is the
-// single pass's extra block: with scan_self it writes the expert offsets and
-// counts (E <= 256 digits), then builds the tile list when asked, while the
-// other blocks scatter.
+// bit.  base[digit, tile] is the row-scanned histogram plus the exclusive
+// scan of the digit totals (k_digit_scan first); or, with scan_self (single
+// pass, few tiles), each block scans the raw histogram itself: its digit's
+// earlier tiles plus all smaller digits.  The last pass also writes the
+// inverse permutation.  Block nb, when launched, is the single pass's extra
+// block: it writes the group offsets and counts (E <= 256 digits), then
+// builds the tile list when asked, while the other blocks scatter.
 template <int ITEMS>
 __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ src, int64_t n, int shift,
     int bits, const int32_t* __restrict__ hist, const int32_t* __restrict__ digit_totals,
     int nb, int32_t* __restrict__ dst, int32_t* __restrict__ inv, int scan_self, int E,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, TileBuild tb) {
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, TileBuild tb, GroupKey gk) {
   __shared__ int32_t run[256];
   __shared__ int32_t wcnt[kRadixThreads / 64][256];
   __shared__ int32_t wsum[4];
@@ -187,7 +162,17 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     start = tid <= mask && (int)blockIdx.x < nb ? hist[(int64_t)tid * nb + blockIdx.x] : 0;
     if (digit_totals) {
       int32_t unused;
-      start += block256_exclusive(tid <= mask ? digit_totals[tid] : 0, wsum, unused);
+      const int32_t tot = tid <= mask ? digit_totals[tid] : 0;
+      const int32_t dbase = block256_exclusive(tot, wsum, unused);
+      start += dbase;
+      if (blockIdx.x == nb && offsets) {  // a single pass's extra block
+        if (tid < E) {
+          offsets[tid] = dbase;
+          counts[tid] = tot;
+        }
+        if (tid == 0) offsets[E] = (int32_t)n;
+        __syncthreads();
+      }
     }
   }
   if (blockIdx.x == nb) {
@@ -207,7 +192,7 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     int dg = 0;
     if (valid) {
       task = src ? src[i] : (int32_t)i;
-      dg = radix_digit(idx, task, shift, mask);
+      dg = radix_digit(idx, task, shift, mask, gk);
     }
     uint64_t same = __ballot(valid);
     for (int b = 0; b < bits; b++) {
@@ -248,7 +233,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ perm,
                                                          int32_t* __restrict__ inv,
-                                                         TileBuild tb) {
+                                                         TileBuild tb, GroupKey gk) {
   __shared__ int32_t cnt[256];
   __shared__ int32_t run[256];
   __shared__ int32_t wcnt[16][256];
@@ -258,7 +243,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
   if (tid < 256) cnt[tid] = 0;
   for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < n; i += 1024) atomicAdd(&cnt[idx[i] & mask], 1);
+  for (int64_t i = tid; i < n; i += 1024) atomicAdd(&cnt[group_of(idx[i], gk) & mask], 1);
   __syncthreads();
   // exclusive scan of the 256 digit counts by the first 4 waves
   if (tid < 256) {
@@ -287,7 +272,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
   for (int64_t base = 0; base < n; base += 1024) {
     const int64_t i = base + tid;
     const bool valid = i < n;
-    const int dg = valid ? (idx[i] & mask) : 0;
+    const int dg = valid ? (group_of(idx[i], gk) & mask) : 0;
     uint64_t same = __ballot(valid);
     for (int b = 0; b < bits; b++) {
       const uint64_t bb = __ballot(valid && ((dg >> b) & 1));
@@ -329,12 +314,12 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
 // result does not depend on their order.
 __global__ void k_segment_offsets(const int32_t* __restrict__ idx, const int32_t* __restrict__ perm,
                                   int64_t n, int E, int bits, int32_t* __restrict__ offsets,
-                                  int32_t* __restrict__ counts) {
+                                  int32_t* __restrict__ counts, GroupKey gk) {
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (p > n) return;
   const int32_t mask = (int32_t)((1u << bits) - 1);
   auto key = [&](int64_t q) {
-    const int32_t e = idx[perm[q]] & mask;
+    const int32_t e = group_of(idx[perm[q]], gk) & mask;
     return e > E ? E : e;
   };
   const int lo = p > 0 ? key(p - 1) : -1;
@@ -354,16 +339,23 @@ int64_t dispatch_scratch_ints(int64_t n, int E) {
   while ((1ll << (8 * passes)) < E) passes++;
   if (passes == 0) passes = 1;
   const int64_t nb = cdiv(n, kRadixTile);
-  // hist (256 * nb); multi-pass sorts add the digit totals and one temp
-  // array of n
-  return 256 * nb + (passes > 1 ? 256 + n : 0);
+  // hist (256 * nb), the digit totals; multi-pass sorts add one temp array
+  // of n
+  return 256 * nb + 256 + (passes > 1 ? n : 0);
 }
 
 bool dispatch_builds_tiles(int64_t n, int E) { return n > 0 && E <= 256; }
 
-hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
+hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E_ids, int width, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* scratch,
                            hipStream_t st, const TileBuild* tb) {
+  // E: the number of groups from here on
+  const int E = (int)cdiv(E_ids, width);
+  GroupKey gk;
+  gk.width = width;
+  gk.wshift = -1;
+  for (int b = 0; b < 31; b++)
+    if ((1 << b) == width) gk.wshift = b;
   int bits = 0;
   while ((1ll << bits) < E) bits++;
   if (bits == 0) bits = 1;  // one expert: a pass on a constant digit keeps task order
@@ -378,7 +370,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     TileBuild none;
     none.tiles = nullptr;
     hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024), 0, st, idx, n, E, bits, counts,
-                       offsets, perm, inv_perm, tb ? *tb : none);
+                       offsets, perm, inv_perm, tb ? *tb : none, gk);
     return hipGetLastError();
   }
   if (bits <= 8) {
@@ -387,21 +379,22 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     int32_t* hist = scratch;
     hipLaunchKernelGGL(k_radix_hist<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
                        (const int32_t*)nullptr, n, 0, bits, hist, nb, (int32_t*)nullptr,
-                       (int64_t)0);
+                       (int64_t)0, gk);
     TileBuild none;
     none.tiles = nullptr;
     const bool build = tb && tb->tiles;
-    // few tiles: every scatter block scans the histogram itself and an extra
-    // block writes offsets and counts; otherwise one scan block first
+    // few tiles: every scatter block scans the histogram itself; otherwise
+    // one block per digit scans its row of tiles first.  The extra block
+    // writes offsets and counts, and builds the tile list (E <= 256 <= its
+    // threads).
     const int scan_self = nb <= kSelfScanTiles;
+    int32_t* totals = hist + 256 * (int64_t)nb;
     if (!scan_self)
-      hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, st, hist,
-                         (int64_t)(1 << bits) * nb, nb, E, n, counts, offsets);
-    // the extra block also builds the tile list (E <= 256 <= its threads)
-    hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb + (scan_self || build ? 1 : 0)),
-                       dim3(kRadixThreads), 0, st, idx, (const int32_t*)nullptr, n, 0, bits, hist,
-                       (const int32_t*)nullptr, nb, perm, inv_perm, scan_self, E, counts, offsets,
-                       build ? *tb : none);
+      hipLaunchKernelGGL(k_digit_scan, dim3(1u << bits), dim3(256), 0, st, hist, nb, totals);
+    hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb + 1), dim3(kRadixThreads), 0, st,
+                       idx, (const int32_t*)nullptr, n, 0, bits, hist,
+                       scan_self ? (const int32_t*)nullptr : (const int32_t*)totals, nb, perm,
+                       inv_perm, scan_self, E, counts, offsets, build ? *tb : none, gk);
     return hipGetLastError();
   }
   // many experts: 8-bit LSD passes (hist, per-digit scan, scatter), then
@@ -421,18 +414,18 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts
     // the first pass also zeroes counts, which the segment kernel accumulates
     hipLaunchKernelGGL(k_radix_hist<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx, src,
                        n, shift, pb, hist, nb, p == 0 ? counts : (int32_t*)nullptr,
-                       p == 0 ? (int64_t)E : (int64_t)0);
+                       p == 0 ? (int64_t)E : (int64_t)0, gk);
     hipLaunchKernelGGL(k_digit_scan, dim3(1u << pb), dim3(256), 0, st, hist, nb, totals);
     TileBuild none;
     none.tiles = nullptr;
     hipLaunchKernelGGL(k_radix_scatter<kRadixItems>, dim3(nb), dim3(kRadixThreads), 0, st, idx,
                        src, n, shift, pb, hist, (const int32_t*)totals, nb, dst,
                        last ? inv_perm : (int32_t*)nullptr, 0, E, (int32_t*)nullptr,
-                       (int32_t*)nullptr, none);
+                       (int32_t*)nullptr, none, gk);
     src = dst;
   }
   hipLaunchKernelGGL(k_segment_offsets, dim3((unsigned)cdiv(n + 1, 256)), dim3(256), 0, st, idx,
-                     perm, n, E, bits, offsets, counts);
+                     perm, n, E, bits, offsets, counts, gk);
   return hipGetLastError();
 }
 

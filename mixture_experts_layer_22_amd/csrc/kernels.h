@@ -98,7 +98,7 @@ hipError_t launch_logits_out(const float* part, int splits, int64_t T, int E, co
 hipError_t launch_select_pk(const float* scores, int splits, int64_t T, int rows, int cols,
                             int krow, int kcol, int k, int32_t* idx, float* gate, hipStream_t st);
 
-// dispatch.hip
+// dispatch.hip: tasks grouped by expert id / width (E groups below)
 int64_t dispatch_scratch_ints(int64_t n, int E);
 // whether launch_dispatch can build a tile list (it does when given one)
 bool dispatch_builds_tiles(int64_t n, int E);
@@ -113,7 +113,9 @@ struct TileBuild {
   int cap1, cap2;
   int64_t T;
 };
-hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E, int32_t* counts,
+// E_ids expert ids in groups of `width`: counts / offsets get
+// ceil(E_ids / width) (+1) entries
+hipError_t launch_dispatch(const int32_t* idx, int64_t n, int E_ids, int width, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* scratch,
                            hipStream_t st,
                            const TileBuild* tb = nullptr);

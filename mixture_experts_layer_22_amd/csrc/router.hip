@@ -36,29 +36,32 @@ __device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uin
 // blocks busy at small T; the selection kernel adds the partials in order z).
 // bf16 x; fp32 W [NL, K].
 //
-// Block: MT tokens (64 or 256) x 64 logits; wave w owns tokens
-// w*MT/4 .. +MT/4 (MT/64 blocks of 16) and all 64 logits (four
-// v_mfma_f32_16x16x32_bf16 tiles per token block).  Per 64-wide K chunk the
-// block's 64 fp32 weight rows are read once, split into their three bf16
-// slices and staged in LDS (24 KB, double buffered), shared by the four
-// waves; x fragments go straight from global memory to registers, one chunk
-// ahead.  The larger block re-splits the weights for 4x the tokens (the
-// product-key layer, with many tokens and no split K).  K is permuted
+// Block: MT tokens (64 with 4 waves, or 256 with 8) x 64 logits; wave w
+// owns tokens w*MT/NW .. +MT/NW (MT/(16 NW) blocks of 16) and all 64 logits
+// (four v_mfma_f32_16x16x32_bf16 tiles per token block).  Per 64-wide K
+// chunk the block's 64 fp32 weight rows are read once, split into their
+// three bf16 slices and staged in LDS (24 KB, double buffered), shared by
+// the waves; x fragments go straight from global memory to registers, one
+// chunk ahead.  The larger block re-splits the weights for 4x the tokens
+// (the product-key layer, with many tokens and no split K).  K is permuted
 // identically for both operands: lane (r = l%16, q = l/16) takes elements
 // [16q, 16q+16) of the chunk, MFMA step h the half [16q + 8h, +8), so each x
 // row is one 128-byte run.  The three slices accumulate into one fp32
 // accumulator.
 __device__ __forceinline__ int rl_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int MT>
-__global__ __launch_bounds__(256) void k_router_logits_bf16(
+template <int MT, int NW>
+__global__ __launch_bounds__(64 * NW) void k_router_logits_bf16(
     const uint16_t* __restrict__ x, int64_t T, int ldx, RouterPart p0, RouterPart p1, int K,
     float* __restrict__ logits, int ldl, int64_t part_stride) {
-  constexpr int MB = MT / 64;  // token blocks of 16 per wave
+  constexpr int NT = 64 * NW;
+  constexpr int MB = MT / (16 * NW);  // token blocks of 16 per wave
+  constexpr int BL = 1024 / NT;       // weight float4 loads per thread per chunk
+  static_assert(MB >= 1 && MB * 16 * NW == MT && BL * NT == 1024, "router tile");
   // [buf][slice * 64 + logit][64 K] bf16, 16-byte chunks swizzled
   __shared__ __attribute__((aligned(16))) uint16_t bs[2][3 * 64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * MT + wave * (MT / 4);
+  const int64_t m0 = (int64_t)blockIdx.x * MT + wave * (MT / NW);
   // blockIdx.y: the first part's logit blocks, then the second's
   const bool second = (int)blockIdx.y >= p0.ny;
   const float* __restrict__ W = second ? p1.W : p0.W;
@@ -77,26 +80,26 @@ __global__ __launch_bounds__(256) void k_router_logits_bf16(
     ap[mb] = x + am * (int64_t)ldx + x_off + kbeg + q * 16;
   }
 
-  // B loader: 64 rows x 16 float4 = 1024 float4, 4 per thread; float4 i of
-  // this thread is row id/16, K elements 4(id%16) .. +3
-  const float* bsrc[4];
-  int bdst[4];
+  // B loader: 64 rows x 16 float4 = 1024 float4, BL per thread; float4 i
+  // of this thread is row id/16, K elements 4(id%16) .. +3
+  const float* bsrc[BL];
+  int bdst[BL];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int id = tid + 256 * i;
+  for (int i = 0; i < BL; i++) {
+    const int id = tid + NT * i;
     const int nl = id >> 4, k4 = (id & 15) * 4;
     const int n = n0 + nl < NL ? n0 + nl : NL - 1;
     bsrc[i] = W + (int64_t)n * K + kbeg + k4;
     bdst[i] = nl * 64 + (((k4 >> 3) ^ rl_swz(nl)) * 8) + (k4 & 7);  // slice 0 position
   }
-  f32x4 breg[4];
+  f32x4 breg[BL];
   auto bload = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) breg[i] = *reinterpret_cast<const f32x4*>(bsrc[i] + c * 64);
+    for (int i = 0; i < BL; i++) breg[i] = *reinterpret_cast<const f32x4*>(bsrc[i] + c * 64);
   };
   auto bstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < BL; i++) {
       uint16_t h[4], m[4], l[4];
 #pragma unroll
       for (int e = 0; e < 4; e++) split3(breg[i][e], h[e], m[e], l[e]);
@@ -207,6 +210,7 @@ __global__ void k_router_logits_f32(const float* __restrict__ x, int64_t T, int 
 // latency once per split).
 constexpr int kMaxRouterSplits = 16;
 __device__ __forceinline__ float sum_parts(const float* p, int nparts, int64_t stride) {
+  if (nparts == 1) return p[0];  // no K split: skips 2 x 15 uniform branches per logit
   float v[kMaxRouterSplits];
 #pragma unroll
   for (int z = 0; z < kMaxRouterSplits; z++) v[z] = z < nparts ? p[z * stride] : 0.f;
@@ -286,7 +290,8 @@ __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ l
 // ------------------------------------------------------------------------
 // Wave-wide selection helpers.  A wave holds up to 64 V (key, id) pairs, V
 // per lane (slot i of lane l).  Keys are fp32 scores mapped to uint32 so
-// that unsigned order is score order; ids are unique.  Rank order is (key
+// that unsigned order is score order; empty slots hold key 0, which no
+// score maps to, so they never count.  Ids are unique.  Rank order is (key
 // descending, id ascending); NaN scores are not supported.
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -294,19 +299,26 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Threshold search of wave_select: the largest th with at least K valid
-// keys >= th, found bit by bit (a key prefix is kept while at least K keys
-// reach it).  Stops early once exactly K keys reach the prefix: those K are
-// then the answer whatever the lower bits.
+// keys >= c over the wave
 template <int V>
-__device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[V], uint32_t valid,
-                                                     int K) {
+__device__ __forceinline__ int count_ge(const uint32_t (&key)[V], uint32_t c) {
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < V; i++) n += __popcll(__ballot(key[i] >= c));
+  return n;
+}
+
+// Threshold search of wave_select: the largest th with at least K keys
+// >= th, found bit by bit (a key prefix is kept while at least K keys reach
+// it).  Stops early once exactly K keys reach the prefix: those K are then
+// the answer whatever the lower bits.  K >= 1 and at least K non-empty
+// slots, so th > 0.
+template <int V>
+__device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[V], int K) {
   uint32_t th = 0;
   for (int b = 31; b >= 0; b--) {
     const uint32_t cand = th | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < V; i++) cnt += __popcll(__ballot(((valid >> i) & 1u) && key[i] >= cand));
+    const int cnt = count_ge<V>(key, cand);
     if (cnt >= K) th = cand;
     if (cnt == K) break;
   }
@@ -316,19 +328,14 @@ __device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[V], u
 // Two threshold searches in one bit loop (two independent chains of
 // ballots and counts; each stops at its own exact count).
 template <int V>
-__device__ __forceinline__ void select_threshold2(const uint32_t (&k0)[V], uint32_t v0, int K0,
-                                                  uint32_t& th0, const uint32_t (&k1)[V],
-                                                  uint32_t v1, int K1, uint32_t& th1) {
+__device__ __forceinline__ void select_threshold2(const uint32_t (&k0)[V], int K0, uint32_t& th0,
+                                                  const uint32_t (&k1)[V], int K1,
+                                                  uint32_t& th1) {
   th0 = th1 = 0;
   bool d0 = false, d1 = false;
   for (int b = 31; b >= 0 && !(d0 && d1); b--) {
     const uint32_t c0 = th0 | (1u << b), c1 = th1 | (1u << b);
-    int n0 = 0, n1 = 0;
-#pragma unroll
-    for (int i = 0; i < V; i++) {
-      n0 += __popcll(__ballot(((v0 >> i) & 1u) && k0[i] >= c0));
-      n1 += __popcll(__ballot(((v1 >> i) & 1u) && k1[i] >= c1));
-    }
+    const int n0 = count_ge<V>(k0, c0), n1 = count_ge<V>(k1, c1);
     if (!d0) {
       if (n0 >= K0) th0 = c0;
       d0 = n0 == K0;
@@ -340,21 +347,20 @@ __device__ __forceinline__ void select_threshold2(const uint32_t (&k0)[V], uint3
   }
 }
 
-// Marks in sel (bit i = slot i) the K best valid pairs given the threshold
-// th of select_threshold: every key above th is taken, and the keys equal
-// to th are taken by ascending id until K are.
+// Marks in sel (bit i = slot i) the K best pairs given the threshold th of
+// select_threshold: every key above th is taken, and the keys equal to th
+// are taken by ascending id until K are.
 template <int V>
-__device__ __forceinline__ uint32_t select_at(const uint32_t (&key)[V], const int (&id)[V],
-                                             uint32_t valid, int K, uint32_t th) {
+__device__ __forceinline__ uint32_t select_at(const uint32_t (&key)[V], const int (&id)[V], int K,
+                                             uint32_t th) {
   uint32_t sel = 0, eq = 0;
   int gt = 0, neq = 0;
 #pragma unroll
   for (int i = 0; i < V; i++) {
-    const bool v = (valid >> i) & 1u;
-    if (v && key[i] > th) sel |= 1u << i;
-    if (v && key[i] == th) eq |= 1u << i;
-    gt += __popcll(__ballot(v && key[i] > th));
-    neq += __popcll(__ballot(v && key[i] == th));
+    if (key[i] > th) sel |= 1u << i;
+    if (key[i] == th) eq |= 1u << i;
+    gt += __popcll(__ballot(key[i] > th));
+    neq += __popcll(__ballot(key[i] == th));
   }
   int need = K - gt;
   if (need >= neq) return sel | eq;
@@ -375,8 +381,8 @@ __device__ __forceinline__ uint32_t select_at(const uint32_t (&key)[V], const in
 
 template <int V>
 __device__ __forceinline__ uint32_t wave_select(const uint32_t (&key)[V], const int (&id)[V],
-                                                uint32_t valid, int K) {
-  return select_at<V>(key, id, valid, K, select_threshold<V>(key, valid, K));
+                                                int K) {
+  return select_at<V>(key, id, K, select_threshold<V>(key, K));
 }
 
 // Position of each selected pair in [0, K): slots in order, lanes in order.
@@ -392,20 +398,48 @@ __device__ __forceinline__ void wave_positions(uint32_t sel, int (&pos)[V]) {
   }
 }
 
-// Sorts one (key, id) pair per lane across the wave, best first (bitonic
-// network; pad lanes with key 0, id INT_MAX).
-__device__ __forceinline__ void wave_sort(uint32_t& key, int& id) {
+// Value of lane l ^ M: DPP quad permutations for M = 1, 2 (no LDS trip),
+// ds_swizzle's xor mode inside 32 lanes for M = 4 .. 16, ds_bpermute for 32.
+template <int M>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  else if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  else if constexpr (M < 32) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10));
+  else return __shfl_xor(v, M, kWave);
+}
+
+// One compare-exchange step of a bitonic sort, best first within blocks
+// of SIZE lanes whose SIZE-bit is clear (the other blocks sort reversed)
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_step(uint32_t& key, int& id, int lane) {
+  const uint32_t ok = (uint32_t)lane_xor<STRIDE>((int)key);
+  const int oi = lane_xor<STRIDE>(id);
+  const bool first = key > ok || (key == ok && id < oi);
+  const bool keep = (((lane & STRIDE) == 0) == ((lane & SIZE) == 0)) ? first : !first;
+  if (!keep) { key = ok; id = oi; }
+}
+
+template <int SIZE>
+__device__ __forceinline__ void bitonic_merge(uint32_t& key, int& id, int lane) {
+  if constexpr (SIZE >= 64) bitonic_step<SIZE, 32>(key, id, lane);
+  if constexpr (SIZE >= 32) bitonic_step<SIZE, 16>(key, id, lane);
+  if constexpr (SIZE >= 16) bitonic_step<SIZE, 8>(key, id, lane);
+  if constexpr (SIZE >= 8) bitonic_step<SIZE, 4>(key, id, lane);
+  if constexpr (SIZE >= 4) bitonic_step<SIZE, 2>(key, id, lane);
+  bitonic_step<SIZE, 1>(key, id, lane);
+}
+
+// Sorts one (key, id) pair per lane, best first, over lanes 0..n-1 (n <=
+// 64; lanes n.. hold pads: key 0, id INT_MAX).  n <= 32 sorts each half of
+// the wave on its own, which leaves lanes 0..31 in order.
+__device__ __forceinline__ void wave_sort(uint32_t& key, int& id, int n) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1)
-#pragma unroll
-    for (int stride = size / 2; stride > 0; stride >>= 1) {
-      const uint32_t ok = __shfl_xor(key, stride, kWave);
-      const int oi = __shfl_xor(id, stride, kWave);
-      const bool first = key > ok || (key == ok && id < oi);
-      const bool keep = (((lane & stride) == 0) == ((lane & size) == 0)) ? first : !first;
-      if (!keep) { key = ok; id = oi; }
-    }
+  bitonic_merge<2>(key, id, lane);
+  bitonic_merge<4>(key, id, lane);
+  bitonic_merge<8>(key, id, lane);
+  bitonic_merge<16>(key, id, lane);
+  bitonic_merge<32>(key, id, lane);
+  if (n > 32) bitonic_merge<64>(key, id, lane);
 }
 
 // ------------------------------------------------------------------------
@@ -432,7 +466,7 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
   const float* srow = scores + t * (int64_t)(rows + cols);
   // step 1: rows and columns, their two threshold searches in one loop
   float v2[2][V];
-  uint32_t key2[2][V], valid2[2] = {0u, 0u};
+  uint32_t key2[2][V];
   int id2[2][V];
 #pragma unroll
   for (int side = 0; side < 2; side++) {
@@ -442,21 +476,17 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
     for (int i = 0; i < V; i++) {
       const int e = lane + 64 * i;
       float sc = -INFINITY;
-      if (e < n) {
-        sc = sum_parts(s + e, nparts, part_stride);
-        valid2[side] |= 1u << i;
-      }
+      if (e < n) sc = sum_parts(s + e, nparts, part_stride);
       v2[side][i] = sc;
-      key2[side][i] = order_key(sc);
+      key2[side][i] = e < n ? order_key(sc) : 0u;
       id2[side][i] = e;
     }
   }
   uint32_t th2[2];
-  select_threshold2<V>(key2[0], valid2[0], krow, th2[0], key2[1], valid2[1], kcol, th2[1]);
+  select_threshold2<V>(key2[0], krow, th2[0], key2[1], kcol, th2[1]);
 #pragma unroll
   for (int side = 0; side < 2; side++) {
-    const uint32_t sel =
-        select_at<V>(key2[side], id2[side], valid2[side], side ? kcol : krow, th2[side]);
+    const uint32_t sel = select_at<V>(key2[side], id2[side], side ? kcol : krow, th2[side]);
     int pos[V];
     wave_positions<V>(sel, pos);
 #pragma unroll
@@ -470,26 +500,22 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   // step 2: candidate scores
   const int nc = krow * kcol;
-  float v[V];
   uint32_t key[V];
   int id[V];
-  uint32_t valid = 0;
 #pragma unroll
   for (int i = 0; i < V; i++) {
     const int c = lane + 64 * i;
     if (c < nc) {
       const int a = c / kcol, b = c - a * kcol;
-      v[i] = sel_val[wave][0][a] + sel_val[wave][1][b];
+      key[i] = order_key(sel_val[wave][0][a] + sel_val[wave][1][b]);
       id[i] = sel_idx[wave][0][a] * cols + sel_idx[wave][1][b];
-      valid |= 1u << i;
     } else {
-      v[i] = -INFINITY;
+      key[i] = 0u;
       id[i] = 0x7fffffff;
     }
-    key[i] = order_key(v[i]);
   }
   // step 3: the k best candidates, gathered in lanes 0..k-1 and sorted
-  const uint32_t sel = wave_select<V>(key, id, valid, k);
+  const uint32_t sel = wave_select<V>(key, id, k);
   int pos[V];
   wave_positions<V>(sel, pos);
 #pragma unroll
@@ -502,15 +528,17 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   uint32_t mk = lane < k ? top_key[wave][lane] : 0u;
   int mi = lane < k ? top_id[wave][lane] : 0x7fffffff;
-  wave_sort(mk, mi);
+  wave_sort(mk, mi, k);
   // back to fp32 scores; gates = softmax over the k (the first is the max)
   const uint32_t bits = (mk & 0x80000000u) ? (mk & 0x7fffffffu) : ~mk;
   const float sv = __uint_as_float(bits);
-  const float top = __shfl(sv, 0, kWave);
+  const float top = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                  __builtin_bit_cast(int, sv)));
   const float e = lane < k ? __expf(sv - top) : 0.f;
-  // the sum in rank order, as the selection loop did it
+  // the sum in rank order (lane broadcasts through scalar registers)
   float gsum = 0.f;
-  for (int j = 0; j < k; j++) gsum += __shfl(e, j, kWave);
+  for (int j = 0; j < k; j++)
+    gsum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), j));
   if (lane < k) {
     idx_out[t * k + lane] = mi;
     gate_out[t * k + lane] = e / gsum;
@@ -536,17 +564,18 @@ hipError_t launch_router_logits(int dtype, const void* x, int64_t T, int ldx, Ro
   p1.ny = (int)cdiv(p1.NL, 64);
   if (p0.ny + p1.ny == 0) return hipSuccess;
   if (dtype == MOE_BF16) {
-    // 256-token blocks when they alone give every CU a block: the weights'
-    // split is then shared by 4x the tokens
+    // 256-token blocks of 8 waves when they alone give every CU a block:
+    // the weights' split is then shared by 4x the tokens, and two waves per
+    // SIMD overlap one's MFMAs with the other's splitting and loads
     const int ny = p0.ny + p1.ny;
     if (splits == 1 && cdiv(T, 256) * ny >= 256) {
       dim3 grid((unsigned)cdiv(T, 256), (unsigned)ny, 1);
-      hipLaunchKernelGGL(k_router_logits_bf16<256>, grid, dim3(256), 0, st, (const uint16_t*)x,
-                         T, ldx, p0, p1, K, logits, ldl, (int64_t)T * ldl);
+      hipLaunchKernelGGL((k_router_logits_bf16<256, 8>), grid, dim3(512), 0, st,
+                         (const uint16_t*)x, T, ldx, p0, p1, K, logits, ldl, (int64_t)T * ldl);
     } else {
       dim3 grid((unsigned)cdiv(T, 64), (unsigned)ny, (unsigned)splits);
-      hipLaunchKernelGGL(k_router_logits_bf16<64>, grid, dim3(256), 0, st, (const uint16_t*)x,
-                         T, ldx, p0, p1, K, logits, ldl, (int64_t)T * ldl);
+      hipLaunchKernelGGL((k_router_logits_bf16<64, 4>), grid, dim3(256), 0, st,
+                         (const uint16_t*)x, T, ldx, p0, p1, K, logits, ldl, (int64_t)T * ldl);
     }
   } else {
     for (const RouterPart& p : {p0, p1})

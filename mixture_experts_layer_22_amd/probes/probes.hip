@@ -1,6 +1,7 @@
-// Ceiling probes (libmoe_probes.so): a streaming read and a memory-free
-// MFMA loop, the measured rates the layer's kernels are set against beside
-// the datasheet peaks.  Only the benchmark and its tests call them.
+// Ceiling probes (libmoe_probes.so): a streaming read, a row gather and a
+// memory-free MFMA loop, the measured rates the layer's kernels are set
+// against beside the datasheet peaks.  Only the benchmark and its tests
+// call them.
 #include "../../include/moe_probes.h"
 #include "../csrc/common.h"
 
@@ -34,6 +35,44 @@ __global__ __launch_bounds__(256) void k_stream_read(const f32x4* __restrict__ b
   if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
   __syncthreads();
   if (threadIdx.x == 0) block_sums[blockIdx.x] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+}
+
+// Row gather: wave w reads the rows idx[w*per .. w*per + per) of a table
+// of 16-byte units (U units per lane and row: lane l takes units l, l+64,
+// ...), 8 rows in flight at a time, and sums them; one partial per wave.
+// Indexes outside [0, n_rows) are clamped.
+template <int U>
+__global__ __launch_bounds__(256) void k_row_gather(const f32x4* __restrict__ table,
+                                                    int64_t n_rows, const int32_t* __restrict__ idx,
+                                                    int64_t n_waves, int per,
+                                                    float* __restrict__ wave_sums) {
+  constexpr int CH = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= n_waves) return;
+  int myrow = 0;
+  if (lane < per) {
+    const int64_t r = idx[w * per + lane];
+    myrow = (int)(r < 0 ? 0 : (r >= n_rows ? n_rows - 1 : r));
+  }
+  float s = 0.f;
+  for (int j0 = 0; j0 < per; j0 += CH) {
+    f32x4 v[CH][U];
+#pragma unroll
+    for (int c = 0; c < CH; c++)
+      if (j0 + c < per) {
+        const f32x4* row = table + (int64_t)__builtin_amdgcn_readlane(myrow, j0 + c) * (64 * U);
+#pragma unroll
+        for (int i = 0; i < U; i++) v[c][i] = row[lane + 64 * i];
+      }
+#pragma unroll
+    for (int c = 0; c < CH; c++)
+      if (j0 + c < per)
+#pragma unroll
+        for (int i = 0; i < U; i++) s += (v[c][i][0] + v[c][i][1]) + (v[c][i][2] + v[c][i][3]);
+  }
+  s = wave_sum(s);
+  if (lane == 0) wave_sums[w] = s;
 }
 
 // 16 independent accumulator chains per wave (started at different values
@@ -78,5 +117,28 @@ extern "C" int32_t moe_probe_mfma_loop(int64_t iters, float* out, int blocks,
   if (iters < 1 || iters > (1 << 19) || blocks < 1 || blocks > 65536) return MOE_ERR_SHAPE;
   hipLaunchKernelGGL(k_mfma_loop, dim3((unsigned)blocks), dim3(512), 0, (hipStream_t)stream,
                      iters, out);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" int32_t moe_probe_row_gather(const void* table, int64_t n_rows, int row_bytes,
+                                        const int32_t* idx, int64_t n_idx, int per_wave,
+                                        float* wave_sums, moe_stream stream) {
+  using namespace moe_probes;
+  if (!table || !idx || !wave_sums) return MOE_ERR_NULL;
+  if (n_rows < 1 || n_idx < 1 || per_wave < 1 || per_wave > 64 || n_idx % per_wave != 0 ||
+      (row_bytes != 1024 && row_bytes != 2048 && row_bytes != 4096 && row_bytes != 8192) ||
+      (uintptr_t)table % 16 != 0)
+    return MOE_ERR_SHAPE;
+  const int64_t n_waves = n_idx / per_wave;
+  if ((n_waves + 3) / 4 > 0x7fffffff) return MOE_ERR_SHAPE;
+  const dim3 grid((unsigned)((n_waves + 3) / 4)), block(256);
+  const f32x4* t = reinterpret_cast<const f32x4*>(table);
+  hipStream_t st = (hipStream_t)stream;
+  switch (row_bytes) {
+    case 1024: hipLaunchKernelGGL(k_row_gather<1>, grid, block, 0, st, t, n_rows, idx, n_waves, per_wave, wave_sums); break;
+    case 2048: hipLaunchKernelGGL(k_row_gather<2>, grid, block, 0, st, t, n_rows, idx, n_waves, per_wave, wave_sums); break;
+    case 4096: hipLaunchKernelGGL(k_row_gather<4>, grid, block, 0, st, t, n_rows, idx, n_waves, per_wave, wave_sums); break;
+    default: hipLaunchKernelGGL(k_row_gather<8>, grid, block, 0, st, t, n_rows, idx, n_waves, per_wave, wave_sums); break;
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

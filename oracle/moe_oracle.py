@@ -173,20 +173,33 @@ def route(cfg, inp):
 
 # ----------------------------------------------------------------- dispatch
 
-def dispatch(idx: np.ndarray, E: int):
+def dispatch_group(cfg) -> int:
+    """Width of a dispatch group: the contiguous range of expert ids whose
+    tasks are collected together ([OMNI] sec. 2.2, Grouping & Sorting).  The
+    page fixes no width; read here as one expert for routed FFN experts (the
+    grouped GEMM's groups) and one row of the expert grid (pk_cols ids) for
+    atomic experts behind the Cartesian-product router."""
+    return int(cfg.pk_cols) if cfg.router == 1 else 1
+
+
+def dispatch(idx: np.ndarray, E: int, group: int = 1):
     """Expert-centric task list ([OMNI] sec. 2.2, Expert-Centric Scheduling).
 
     Task collection: the batch's routing decisions flattened to tasks
     tau = t*k + j with expert idx[t, j].  Grouping & sorting: tasks grouped by
-    expert id in increasing order and, inside a group, by token id -- a
-    stable sort of the task ids by expert.  Zero-computation experts have the
-    highest ids, so their tasks form the tail segments.
-    Returns counts [E], offsets [E+1], perm [T*k] (task id at each sorted
-    position) and inv_perm (sorted position of each task), all int32.
+    contiguous ranges of `group` expert ids (group g holds ids
+    [g*group, (g+1)*group)), groups in increasing order, and inside a group
+    by token id -- a stable sort of the task ids by idx // group (task ids
+    already run in token order).  Zero-computation experts have the highest
+    ids, so their tasks form the tail segments.
+    Returns counts [G], offsets [G+1] (G = ceil(E / group) groups), perm
+    [T*k] (task id at each sorted position) and inv_perm (sorted position of
+    each task), all int32.
     """
     flat = idx.reshape(-1).astype(np.int64)
-    perm = np.argsort(flat, kind="stable")
-    counts = np.bincount(flat, minlength=E)
+    key = flat // group
+    perm = np.argsort(key, kind="stable")
+    counts = np.bincount(key, minlength=-(-E // group))
     offsets = np.concatenate([[0], np.cumsum(counts)])
     inv_perm = np.empty_like(perm)
     inv_perm[perm] = np.arange(perm.size)
@@ -319,7 +332,8 @@ def forward(cfg, inp, idx=None, gate=None, tokens=None):
         idx, gate, _ = route(cfg, inp)
     idx = np.asarray(idx, dtype=np.int32)
     gate = np.asarray(gate, dtype=np.float64)
-    counts, offsets, perm, inv_perm = dispatch(idx, cfg.E)
+    grp = dispatch_group(cfg)
+    counts, offsets, perm, inv_perm = dispatch(idx, cfg.E, grp)
     T, k = idx.shape
     if tokens is not None:
         tokens = np.asarray(tokens)
@@ -331,7 +345,8 @@ def forward(cfg, inp, idx=None, gate=None, tokens=None):
         sub_perm = perm[pos]
         sub_inv = np.full(T * k, -1, dtype=np.int64)
         sub_inv[sub_perm] = np.arange(sub_perm.size)
-        sub_idx_counts = np.bincount(idx.reshape(-1)[sub_perm], minlength=cfg.E)
+        sub_idx_counts = np.bincount(idx.reshape(-1)[sub_perm] // grp,
+                                     minlength=-(-cfg.E // grp))
         sub_off = np.concatenate([[0], np.cumsum(sub_idx_counts)])
         perm_use, inv_use, off_use = sub_perm, sub_inv, sub_off
     else:

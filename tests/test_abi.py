@@ -273,6 +273,15 @@ def test_probes_reject_on_host(prb):
     assert mfma(0, P, 4, None) == B.MOE_ERR_SHAPE
     assert mfma((1 << 19) + 1, P, 4, None) == B.MOE_ERR_SHAPE
     assert mfma(10, P, 0, None) == B.MOE_ERR_SHAPE
+    gather = prb.moe_probe_row_gather
+    assert gather(None, 8, 2048, P, 32, 32, P, None) == B.MOE_ERR_NULL
+    assert gather(P, 8, 2048, None, 32, 32, P, None) == B.MOE_ERR_NULL
+    assert gather(P, 8, 2048, P, 32, 32, None, None) == B.MOE_ERR_NULL
+    assert gather(P, 0, 2048, P, 32, 32, P, None) == B.MOE_ERR_SHAPE
+    assert gather(P, 8, 3000, P, 32, 32, P, None) == B.MOE_ERR_SHAPE    # row size
+    assert gather(P, 8, 2048, P, 33, 32, P, None) == B.MOE_ERR_SHAPE    # n_idx % per_wave
+    assert gather(P, 8, 2048, P, 65 * 2, 65, P, None) == B.MOE_ERR_SHAPE  # per_wave > 64
+    assert gather(P + 4, 8, 2048, P, 32, 32, P, None) == B.MOE_ERR_SHAPE  # misaligned
 
 
 def test_noalloc_rejects_on_host(lib):

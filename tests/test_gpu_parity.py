@@ -68,7 +68,7 @@ def test_small_stagewise(name):
 
     y, sy = layer.expert_ffn(x, idx, perm, offsets)
     torch.cuda.synchronize()
-    _, o_off, o_perm, o_inv = O.dispatch(idx_np, cfg.E)
+    _, o_off, o_perm, o_inv = O.dispatch(idx_np, cfg.E, O.dispatch_group(cfg))
     tol = C.out_tol(cfg)
     if cfg.router == I.ROUTER_PRODUCT_KEY:
         h_ref = O.atomic_h(cfg, inp, idx_np, o_perm)

@@ -1,6 +1,8 @@
 """The ceiling probes on the GPU: the streaming read must read every
-element once (its sums are exact on a buffer of ones), and the MFMA loop
-must run every MFMA (its accumulators end at exactly 32 per round)."""
+element once (its sums are exact on a buffer of ones), the row gather must
+read every listed row whole (its per-wave sums are exact on small integer
+rows), and the MFMA loop must run every MFMA (its accumulators end at
+exactly 32 per round)."""
 import numpy as np
 import pytest
 import torch
@@ -28,3 +30,23 @@ def test_mfma_loop_runs_every_round(iters, blocks):
     B.moe_probe_mfma_loop(iters, out, blocks)
     torch.cuda.synchronize()
     assert (out.cpu().numpy() == 32.0 * iters).all()
+
+
+@pytest.mark.parametrize("row_bytes,per,n_waves", [(1024, 1, 5), (2048, 32, 37), (8192, 13, 9)])
+def test_row_gather_reads_every_row(row_bytes, per, n_waves):
+    n_rows = 300
+    rf = row_bytes // 4
+    rng = np.random.default_rng(row_bytes + per)
+    # row r holds r in every float but one marked element, so a skipped unit
+    # or row changes the sum
+    table = np.repeat(np.arange(n_rows, dtype=np.float32)[:, None], rf, axis=1)
+    table[:, rf // 3] += 1.0
+    idx = rng.integers(0, n_rows, size=n_waves * per).astype(np.int32)
+    idx[0] = n_rows + 5   # clamped to the last row
+    sums = torch.full((n_waves,), -1.0, dtype=torch.float32, device="cuda")
+    B.moe_probe_row_gather(torch.from_numpy(table).cuda(), n_rows, row_bytes,
+                           torch.from_numpy(idx).cuda(), idx.size, per, sums)
+    torch.cuda.synchronize()
+    rows = np.clip(idx, 0, n_rows - 1).astype(np.float64).reshape(n_waves, per)
+    want = (rows * rf + 1.0).sum(axis=1)
+    assert np.array_equal(sums.cpu().numpy().astype(np.float64), want)

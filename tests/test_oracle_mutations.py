@@ -72,10 +72,10 @@ def _const_swapped(X64, wc, v, _orig=O.constant_expert):
     return _orig(X64, np.asarray(wc)[::-1], v)
 
 
-def _dispatch_unstable(idx, E, _orig=O.dispatch):
-    counts, offsets, perm, inv = _orig(idx, E)
+def _dispatch_unstable(idx, E, group=1, _orig=O.dispatch):
+    counts, offsets, perm, inv = _orig(idx, E, group)
     perm = perm.copy()
-    for e in range(E):
+    for e in range(len(counts)):
         perm[offsets[e]:offsets[e + 1]] = perm[offsets[e]:offsets[e + 1]][::-1]
     inv = np.empty_like(perm)
     inv[perm] = np.arange(perm.size)

@@ -326,6 +326,30 @@ def test_dispatch_invariants_and_buckets():
     assert np.array_equal(np.bincount(perm // k, minlength=T), np.full(T, k))
 
 
+def test_dispatch_groups_of_expert_ranges():
+    """Groups of contiguous id ranges (OmniMoE page sec. 2.2, Grouping &
+    Sorting): brute force on a tiny batch -- the task list ordered by the
+    tuple (id // width, token, slot) with Python's sort -- and the product-
+    key layer's width is one row of its expert grid."""
+    rng = np.random.default_rng(12)
+    T, k, E = 23, 4, 24
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    for width in (1, 5, 8, 24):
+        counts, offsets, perm, inv = O.dispatch(idx, E, width)
+        G = -(-E // width)
+        tasks = sorted(range(T * k), key=lambda tau: (idx[tau // k, tau % k] // width,
+                                                      tau // k, tau % k))
+        assert list(perm) == tasks
+        assert counts.size == G and offsets.size == G + 1
+        assert list(counts) == [sum(1 for tau in range(T * k)
+                                    if idx[tau // k, tau % k] // width == g) for g in range(G)]
+        assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+        assert np.array_equal(inv[perm], np.arange(T * k))
+    cfg = I.small_variant("atomic-pk")
+    assert O.dispatch_group(cfg) == cfg.pk_cols
+    assert O.dispatch_group(I.small_variant("moepp")) == 1
+
+
 def test_dispatch_empty_and_single_expert():
     counts, offsets, perm, inv = O.dispatch(np.zeros((0, 2), np.int32), 4)
     assert perm.size == 0 and list(offsets) == [0, 0, 0, 0, 0]
