@@ -287,20 +287,43 @@ def token_centric_ablation(args, torch, B, I):
         B.moe_ablation_atomic_token_centric(layer.dims, layer.weights, x, T, idx, gate, out,
                                             stream)
     torch.cuda.synchronize()
-    # expert-centric: phases after routing, from traced forwards
+    # expert-centric: the kernels after routing through the stage entry
+    # points (dispatch, activations, combine: the same launches as the
+    # forward's, without phase markers); the phases of traced forwards
+    # are reported beside it
     ph = traced_phases(torch, B, stream, lambda ev: B.moe_forward_traced(
         layer.dims, layer.weights, x, T, out, ws, ev, stream=stream), max(1, min(args.steps, 20)))
-    ec_us = sum(v for k, v in ph.items() if k != "route")
-    # token-centric: the one kernel
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
+    n = T * cfg.k
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    inv = torch.empty(n, dtype=torch.int32, device=dev)
+    h = torch.empty(n, dtype=torch.float32, device=dev)
+
+    def expert_centric():
+        B.moe_dispatch(layer.dims, idx, T, counts, offsets, perm, inv, ws, stream)
+        B.moe_expert_ffn(layer.dims, layer.weights, x, T, idx, perm, offsets, h, None, ws,
+                         stream)
+        B.moe_combine(layer.dims, layer.weights, x, T, idx, gate, inv, h, None, out, stream)
+
+    def token_centric():
         B.moe_ablation_atomic_token_centric(layer.dims, layer.weights, x, T, idx, gate, out,
                                             stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    tc_us = 1e3 * e0.elapsed_time(e1) / args.steps
+
+    def per_step_us(fn):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / args.steps
+
+    ec_us = per_step_us(expert_centric)
+    tc_us = per_step_us(token_centric)
     print(json.dumps({
         "metric": "atomic_expert_centric_vs_token_centric",
         "expert_centric_us": ec_us, "expert_centric_phases_us": ph,
