@@ -30,17 +30,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if there is none or the kernel's source changed since."""
+    """HBM bytes per launch of a stage kernel from the committed counter
+    summary of the workload (one record, or a list under "records"), or
+    None if there is none for the kernel or its source changed since."""
     from mixture_experts_layer_22_amd import profiling as P
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     try:
-        rec = json.load(open(path))
+        data = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel") != kernel or rec.get("source_sha256") != P.kernel_source_sha(kernel):
-        return None
-    return rec.get("bytes")
+    for rec in data.get("records", [data]):
+        if rec.get("kernel") == kernel and rec.get("source_sha256") == P.kernel_source_sha(kernel):
+            return rec.get("bytes")
+    return None
 
 
 def log(*a):

@@ -171,7 +171,7 @@ def main(argv=None):
     s.add_argument("--cmd", default="")
     s.add_argument("--log", help="the profiled bench run's output (for its phase times)")
     t = sub.add_parser("traffic")
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", action="append", required=True)
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--fetch", required=True)
@@ -202,11 +202,12 @@ def main(argv=None):
         if a.cmd:
             text = f"command: {a.cmd}\n\n{text}\n"
     else:
-        rec = traffic_record(a.kernel, a.copy_fetch, a.copy_write, a.fetch, a.write, a.copy_bytes,
-                             a.copy_kernel)
+        recs = [traffic_record(k, a.copy_fetch, a.copy_write, a.fetch, a.write, a.copy_bytes,
+                               a.copy_kernel) for k in a.kernel]
+        out = {"records": recs}
         if a.cmd:
-            rec["command"] = a.cmd
-        text = json.dumps(rec, indent=1)
+            out["command"] = a.cmd
+        text = json.dumps(out, indent=1)
     if a.out:
         with open(a.out, "w") as f:
             f.write(text + ("\n" if not text.endswith("\n") else ""))

@@ -132,6 +132,14 @@ def test_traffic_record_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch
     (tmp_path / "traffic_w.json").write_text(json.dumps(rec))
     assert bench.measured_traffic("w", kernel) is None
     assert bench.measured_traffic("missing", kernel) is None
+    # several kernels' records in one summary
+    k2 = "k_gemm_dl<false>"
+    recs = [{"kernel": kernel, "bytes": 5.0, "source_sha256": P.kernel_source_sha(kernel)},
+            {"kernel": k2, "bytes": 7.0, "source_sha256": P.kernel_source_sha(k2)}]
+    (tmp_path / "traffic_w.json").write_text(json.dumps({"records": recs}))
+    assert bench.measured_traffic("w", kernel) == 5.0
+    assert bench.measured_traffic("w", k2) == 7.0
+    assert bench.measured_traffic("w", "k_atomic_h<unsigned short>") is None
 
 
 def _counter_csv(path, rows):

@@ -310,10 +310,35 @@ def test_uneven_down_projection_items(T, E, k, f, n_shared, f_shared):
     _forward_vs_oracle(cfg, I.make_inputs(cfg))
 
 
+@pytest.mark.parametrize("T,E,k,d,f,hot", [
+    (16, 128, 8, 2048, 768, False),  # the decode layer's shape
+    (5, 32, 2, 640, 320, False),     # K not a multiple of 512; partial column tiles
+    (24, 64, 4, 256, 192, True),     # one expert takes every token: a 24-row group
+    (7, 16, 3, 4096, 128, False),    # rows of 4096 (eight units per lane)
+])
+def test_decode_small_groups(T, E, k, d, f, hot):
+    """Decode-sized layers (fewer than 64 tasks per expert) run the 32-row
+    tile kernel, whose K tiles stream two deep through registers: K not a
+    multiple of its 64-wide tile's 512 B, partial column tiles, one group of
+    24 rows, and K = 4096 (64 tiles)."""
+    assert T * k < 64 * E   # the 32-row path
+    cfg = I.small_variant("qwen3-decode").replace(T=T, E=E, E_ffn=E, k=k, d=d, f=f,
+                                                  n_shared=0, seed=21)
+    inp = I.make_inputs(cfg)
+    if hot:
+        b = np.zeros(cfg.E, np.float32)
+        b[5] = 50.0
+        inp["router_bias"] = b
+    say("decode small groups", T, E, k, d, f, hot)
+    _, _, _, idx_np = _forward_vs_oracle(cfg, inp)
+    if hot:
+        assert np.all(idx_np[:, 0] == 5)
+
+
 @pytest.mark.parametrize("T,E,k", [(9000, 16, 8), (20000, 200, 4)])
 def test_dispatch_with_many_tiles(T, E, k):
     """One-pass dispatch with more than 64 histogram tiles of 1024 tasks
-    (72,000 and 80,000 tasks): the path with a separate scan block, checked
+    (72,000 and 80,000 tasks): the path with a per-digit scan launch, checked
     bit-exact through the dispatch entry point and end to end on a sample of
     tokens."""
     cfg = I.small_variant("deepseek16b").replace(T=T, d=64, E=E, E_ffn=E, k=k, f=64,
