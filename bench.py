@@ -25,7 +25,7 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (datasheet)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (datasheet)
 METRIC = "MoE layer tokens/sec at 1 GPU; % of bf16 MFMA peak or HBM GB/s"
 COPY_BYTES = 1 << 30
-COLD_BYTES = 512 << 20         # written before each cold step: twice the 256 MB MALL
+COLD_BYTES = 512 << 20         # read before each cold step: twice the 256 MB MALL
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -106,7 +106,8 @@ def stage_kernels(cfg):
         if cfg.n_shared:
             out.append(("gemm1", "k_gemm_dl<true>", "mfma", "gemm1_flop"))
             out.append(("gemm2", "k_gemm_dl<false>", "mfma", "gemm2_flop"))
-        out.append(("combine", "k_atomic_combine<%s>" % t, "hbm", "atomic_combine_bytes"))
+        u = next(v for v in (1, 2, 4, 8, 16) if cfg.d <= 512 * v)  # 16-byte units per lane
+        out.append(("combine", f"k_atomic_combine<{t}, {u}>", "hbm", "atomic_combine_bytes"))
         return out
     if cfg.dtype != 1:
         return [("gemm1", "k_grouped_gemm_f32<true>", "hbm", "gemm1_bytes"),
@@ -121,7 +122,7 @@ def stage_kernels(cfg):
 
 def rooflines(cfg, work, phase_warm, phase_cold):
     """One roofline record per expert-stage kernel.  An HBM-bound kernel is
-    rated on steps that each follow a 512 MiB write (nothing of the layer in
+    rated on steps that each follow a 512 MiB read (nothing of the layer in
     the MALL or the L2s); an MFMA-bound one on warm steps (its weights
     exceed the MALL anyway); both fractions are kept.  The headline record
     is the kernel with the longest measured phase."""
@@ -195,11 +196,30 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
 TAUS = (1.0, 0.75, 0.5, 0.25, 0.1)
 
 
+class Evictor:
+    """Cold caches before a step: a streaming read of a 512 MiB buffer of
+    its own (twice the 256 MB MALL), so none of the layer's data is left in
+    the MALL or the L2s.  A read, not a write: a written buffer would leave
+    about 256 MB of dirty lines whose write-back then competes with the
+    step's own reads (measured: a 509 MB weight stream ran 147-160 us after
+    a 512 MiB write and 90-104 us after a 512 MiB read, as warm)."""
+
+    def __init__(self, torch, B, stream, dev):
+        self.B, self.stream = B, stream
+        self.n = COLD_BYTES // 4
+        self.buf = torch.ones(self.n, dtype=torch.float32, device=dev)
+        self.sums = torch.empty(4096, dtype=torch.float32, device=dev)
+        self()                      # the fill's dirty lines go out here
+        torch.cuda.synchronize()
+
+    def __call__(self, i=0):
+        self.B.moe_probe_stream_read(self.buf, self.n, self.sums, 4096, self.stream)
+
+
 def traced_phases(torch, B, stream, step_traced, n, evict=None):
     """Mean device time of each phase (us) over n steps bracketed by the
     library's phase events, recorded on the stream the kernels run on.  With
-    `evict`, a 512 MiB write precedes each step, so none of the layer's data
-    is left in the MALL or the L2s."""
+    `evict` (an Evictor), each step starts with cold caches."""
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_PHASES + 1)]
            for _ in range(n)]
     for row in evs:                     # materialise the lazily created events
@@ -208,7 +228,7 @@ def traced_phases(torch, B, stream, step_traced, n, evict=None):
     torch.cuda.synchronize()
     for i in range(n):
         if evict is not None:
-            evict.fill_(float(i))
+            evict(i)
         step_traced(evs[i])
     torch.cuda.synchronize()
     return {name: 1e3 * float(np.mean([evs[i][p].elapsed_time(evs[i][p + 1])
@@ -426,18 +446,18 @@ def main():
     n_traced = max(1, min(args.steps, 20))
     log(f"[bench] traced steps {n_traced} warm, {n_traced} cold")
     phase_us = traced_phases(torch, B, stream, step_traced, n_traced)
-    scratch = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device=dev)
+    scratch = Evictor(torch, B, stream, dev)
     phase_cold_us = traced_phases(torch, B, stream, step_traced, n_traced, scratch)
 
     # per-step spread: steps bracketed one by one, warm, then cold (a 512 MiB
-    # write before each step); the per-step events add a little time of
+    # read before each step); the per-step events add a little time of
     # their own
     def step_times(n, evict=None):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
         for i, (a, b) in enumerate(ev):
             if evict is not None:
-                evict.fill_(float(i))
+                evict(i)
             a.record(stream)
             step()
             b.record(stream)

@@ -102,7 +102,7 @@ def test_roofline_picks_the_longest_stage_and_rates_hbm_kernels_cold():
     head, recs = bench.rooflines(atom, work, _phases(atomic=1.0, combine=1.5),
                                  _phases(atomic=4.0, combine=2.0))
     assert [r["kernel"] for r in recs] == ["k_atomic_h<unsigned short>",
-                                          "k_atomic_combine<unsigned short>"]
+                                          "k_atomic_combine<unsigned short, 2>"]
     assert head["kernel"] == "k_atomic_h<unsigned short>" and head["timing"] == "cold"
     assert head["achieved"] == 100e9 / 4e-6 / 1e9 and head["frac_warm"] == 100e9 / 1e-6 / 1e9 / 8000
     moepp = I.CONFIGS["moepp"]
