@@ -12,13 +12,12 @@
 // columns' W_up rows, and each wave's fragments pair gate and up columns, so
 // silu(g)*u is formed in registers and H is written once, in bf16.
 //
-// Three kernels: k_gemm_dl (bf16, groups of 64 rows or more: 8 waves,
-// v_mfma_f32_16x16x32_bf16, a five-stage direct-to-LDS K pipeline; the main
-// path), k_grouped_gemm_bf16 (decode-sized groups: 32-row tiles,
-// v_mfma_f32_32x32x16_bf16, K tiles of 64 in one LDS buffer with the next
-// staged in registers, 16-byte chunk c of a 128-byte row at c ^ (row & 7)),
-// and
-// k_grouped_gemm_f32 (fp32 layers, plain FMA).
+// Three kernels: k_gemm_dl (bf16 items of up to 256 rows: 8 waves,
+// v_mfma_f32_16x16x32_bf16, 64-wide K tiles in a 20-slot direct-to-LDS
+// ring; the main path), k_grouped_gemm_bf16 (decode-sized groups: 32-row
+// tiles, v_mfma_f32_32x32x16_bf16, K tiles of 64 in one LDS buffer with the
+// next staged in registers, 16-byte chunk c of a 128-byte row at
+// c ^ (row & 7)), and k_grouped_gemm_f32 (fp32 layers, plain FMA).
 #include <type_traits>
 
 #include "kernels.h"
@@ -266,10 +265,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
 // bf16 MFMA grouped GEMM, BMT x 256 (B rows) tiles, direct-to-LDS pipeline.
 //
 // Global -> LDS copies use global_load_lds_dwordx4 (no staging registers):
-// lane i of a wave lands 16 bytes at LDS base + 16 i.  K advances in 32-wide
-// tiles held in a ring of five LDS stages of 32 KB (A rows [0, 256), B rows
-// [256, 512), 64 B per row), i.e. all 160 KB of the CU's LDS.  A K tile is
-// one v_mfma_f32_16x16x32_bf16 step.
+// lane i of a wave lands 16 bytes at LDS base + 16 i, so a swizzled LDS
+// layout comes from permuting the lanes' source addresses.
 //
 // Eight waves, two per SIMD, each owning BMT/2 rows x 64 B rows (128
 // accumulator registers).  On CDNA4 the 32x32x16 MFMA shape stalls the
@@ -278,18 +275,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
 // 16x16x32 shape with two waves per SIMD keeps the copies and the MFMAs
 // overlapped (measured: the same copy + MFMA mix runs in 0.7x the time).
 //
-// One barrier per K tile: it publishes tile t+1 (each wave first waits for
-// its own copies) and certifies that every wave holds tile t's fragments, so
-// tile t's stage takes tile t+5 right away: copies run four K tiles ahead.
-//
-// LDS rows are 4 chunks of 16 B; chunk c of row r sits at c ^ f(r),
-// f(r) = ((r >> 1) & 3) ^ ((r >> 2) & 3).  A fragment read (16 consecutive
-// rows x 4 chunks, 1 KB) touches distinct banks within every 16 lanes.
-//
 // Rows past the group's end (A) or past N (B) are pointed at a valid row:
 // their products only reach output rows / columns that are not stored.
-__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 2) & 3); }
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
@@ -302,18 +289,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// vmcnt(n * L) for a wave-uniform n in [0, 4]
-template <int L>
-__device__ __forceinline__ void wait_vmcnt_tiles(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<L>(); break;
-    case 2: wait_vmcnt<2 * L>(); break;
-    case 3: wait_vmcnt<3 * L>(); break;
-    default: wait_vmcnt<4 * L>(); break;
-  }
 }
 
 constexpr int kGemmLdsElems = 81920;  // 160 KB: all of the CU's LDS
@@ -381,164 +356,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const TileCt
     const uint4 w = (r & 1) ? make_uint4(v.z, v.w, v.x, v.y) : v;
     *reinterpret_cast<uint4*>(c_row<uint16_t, SWIGLU>(args, c, r) + col) = w;
   }
-}
-
-// One tile of BMT (64, 128, 192 or 256) rows x 256 B rows.  Waves form a
-// 2 (rows) x 4 (B rows) grid; a wave owns BMT/2 rows in FM = BMT/32 blocks
-// of 16 and 64 B rows in 4 blocks of 16 (for the gated GEMM: 32 gate rows
-// and the same 32 columns' up rows).
-template <int BMT, bool SWIGLU>
-__device__ __forceinline__ void gemm_tile_dl(const GemmArgs& args, const TileCtx<SWIGLU>& c,
-                                             int n0, uint16_t* lds) {
-  constexpr int BN = 256, BK = 32;
-  constexpr int RA = 256;                    // LDS rows of A; B rows follow
-  constexpr int NS = 5;                      // stages in the ring
-  constexpr int STAGE = (RA + BN) * BK;
-  constexpr int NW = kGemmThreads / 64;
-  constexpr int FM = BMT / 32, FN = 4;
-  constexpr int CA = BMT / 16;               // A copies (16 rows x 64 B) per K tile
-  constexpr int CT = CA + BN / 16;           // all copies of a K tile
-  constexpr int LMAX = (CT + NW - 1) / NW;   // copies per wave per K tile: LMIN or LMAX
-  constexpr int LMIN = CT / NW;
-  static_assert(NS * STAGE <= kGemmLdsElems && BMT % 64 == 0 && BMT <= RA, "LDS ring");
-  static_assert(4 * LMAX < 64, "vmcnt range");
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-
-  // loader: this wave's copy i is block copy j = wave + NW*i (if j < CT);
-  // j < CA covers A rows j*16 + lane/4, the rest B rows (j-CA)*16 + lane/4;
-  // the lane's 16 B is logical chunk (lane & 3) ^ f(row) of the row's 64-byte
-  // K slice.  Waves with fewer copies wait with the smaller count (a wait
-  // for more of their own copies than needed, never fewer).
-  const uint16_t* src[LMAX];
-#pragma unroll
-  for (int i = 0; i < LMAX; i++) {
-    int j = wave + NW * i;
-    if (j >= CT) j = CT - 1;  // unused
-    const bool isa = j < CA;
-    const int r = (isa ? j : j - CA) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ lds_swz(r);
-    const uint16_t* p;
-    if (isa) {
-      p = a_row<uint16_t, SWIGLU>(args, c, r);
-      if (!p) p = a_row<uint16_t, SWIGLU>(args, c, 0);
-    } else {
-      p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, r);
-      if (!p) p = b_row<uint16_t, SWIGLU, BN>(args, c, n0, SWIGLU && r >= BN / 2 ? BN / 2 : 0);
-    }
-    src[i] = p + chunk * 8;
-  }
-  // shared group of the down projection: K slices in separate blocks (the
-  // delta is 0 elsewhere)
-  const int64_t seg_step = c.shared ? args.b_seg_shared - args.k_seg_shared : 0;
-  const int seg_tiles = c.shared ? args.k_seg_shared / BK : 1;
-  auto copy_one = [&](int t, int stage, int i) {
-    const int j = wave + NW * i;
-    if (j < CT) {
-      const int row0 = j < CA ? j * 16 : RA + (j - CA) * 16;
-      const int64_t bdel = (j >= CA && seg_step) ? (int64_t)(t / seg_tiles) * seg_step : 0;
-      dl_copy16(src[i] + t * BK + bdel, lds + stage * STAGE + row0 * BK);
-    }
-  };
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; i++)
-#pragma unroll
-    for (int j = 0; j < FN; j++) acc[i][j] = f32x4{};
-
-  int brow[FN];
-#pragma unroll
-  for (int fn = 0; fn < FN; fn++)
-    brow[fn] = SWIGLU ? (fn < 2 ? wn * 32 + fn * 16 : BN / 2 + wn * 32 + (fn - 2) * 16)
-                      : wn * 64 + fn * 16;
-  const int frow = lane & 15;
-  const int fch = ((lane >> 4) ^ lds_swz(frow)) * 8;
-  const int nk = c.K / BK;
-
-  // Fragments, single-buffered: afr[fm] is refilled with the next tile's
-  // fragment once the 4 MFMAs of row fm are issued, the B fragments after
-  // the last row (the other wave on the SIMD covers the wait for them).  The
-  // compiler's own lgkmcnt waits order each read before its first use.
-  bf16x8 afr[FM];
-  bf16x8 bfr[FN];
-  auto read_a = [&](int stage, int fm) {
-    const int row = wm * (BMT / 2) + fm * 16 + frow;
-    afr[fm] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + fch);
-  };
-  auto read_b = [&](int stage, int fn) {
-    const int row = RA + brow[fn] + frow;
-    bfr[fn] = *reinterpret_cast<const bf16x8*>(lds + stage * STAGE + row * BK + fch);
-  };
-  auto mfma_row = [&](int fm) {  // the 4 MFMAs of fragment row fm
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++)
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], afr[fm], acc[fm][fn], 0, 0, 0);
-  };
-  constexpr int CPR = (LMAX + FM - 2) / (FM > 1 ? FM - 1 : 1);  // copies per row after the barrier
-
-  // One K tile (in `stage`).  Row 0 multiplies before the barrier (this
-  // wave's reads of the tile have then had a row of MFMAs to land); after
-  // it, rows 1.. issue tile ct's copies into the freed stage and read tile
-  // t+1's A fragments from stage nst, its B fragments after the last row.
-  auto tile = [&](bool more, bool copy, int ct, int cst, int nst, auto wait_fn) {
-    mfma_row(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      wait_fn();                            // this wave's copies of tile t+1 ...
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // ... and reads of tile t (lgkmcnt(0))
-      __builtin_amdgcn_s_barrier();         // ... and everyone's; tile t fully read
-    }
-#pragma unroll
-    for (int fm = 1; fm <= FM; fm++) {
-      if (fm < FM) mfma_row(fm);
-      if (copy)
-#pragma unroll
-        for (int i = (fm - 1) * CPR; i < fm * CPR && i < LMAX; i++)
-          if (FM > 1 || fm == 1) copy_one(ct, cst, i);
-      if (more) {
-        if (fm == 1) read_a(nst, 0);
-        if (fm < FM) read_a(nst, fm);
-        if (fm == FM)
-#pragma unroll
-          for (int fn = 0; fn < FN; fn++) read_b(nst, fn);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // prologue: tiles 0 .. NS-1 in flight (tile t in stage t), tile 0
-  // published, its fragments in registers
-  const int pro = nk < NS ? nk : NS;
-#pragma unroll 1
-  for (int t = 0; t < pro; t++)
-#pragma unroll
-    for (int i = 0; i < LMAX; i++) copy_one(t, t, i);
-  wait_vmcnt_tiles<LMIN>(pro - 1);
-  __builtin_amdgcn_s_barrier();
-#pragma unroll
-  for (int fm = 0; fm < FM; fm++) read_a(0, fm);
-#pragma unroll
-  for (int fn = 0; fn < FN; fn++) read_b(0, fn);
-
-  int st = 0;  // stage of tile t
-  int t = 0;
-  auto next = [](int x) { return x == NS - 1 ? 0 : x + 1; };
-  // steady state: tile t+NS exists
-  for (; t + NS < nk; t++) {
-    tile(true, true, t + NS, st, next(st), [] { wait_vmcnt<(NS - 2) * LMIN>(); });
-    st = next(st);
-  }
-  // drain: every copy is issued; tiles after t+1 left in flight: nk-2-t
-  for (; t < nk; t++) {
-    const int left = nk - 2 - t;
-    tile(t + 1 < nk, false, 0, 0, next(st), [&] { wait_vmcnt_tiles<LMIN>(left); });
-    st = next(st);
-  }
-
-  gemm_epilogue<BMT, SWIGLU, FM, FN>(args, c, n0, lds, acc, wm, wn);
 }
 
 // vmcnt(n) for a wave-uniform n in [0, 20]
