@@ -234,16 +234,27 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
                                                          int32_t* __restrict__ perm,
                                                          int32_t* __restrict__ inv,
                                                          TileBuild tb, GroupKey gk) {
+  constexpr int kPer = kSmallDispatch / 1024;  // tasks per thread
   __shared__ int32_t cnt[256];
   __shared__ int32_t run[256];
+  __shared__ int32_t off[257];  // the offsets, for the tile list
   __shared__ int32_t wcnt[16][256];
   __shared__ int32_t wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int mask = (1 << bits) - 1;
   if (tid < 256) cnt[tid] = 0;
   for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+  // this thread's tasks' digits, loaded once (task tid + 1024 r)
+  int dgs[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; r++) {
+    const int64_t i = tid + 1024 * r;
+    dgs[r] = i < n ? (group_of(idx[i], gk) & mask) : 0;
+  }
   __syncthreads();
-  for (int64_t i = tid; i < n; i += 1024) atomicAdd(&cnt[group_of(idx[i], gk) & mask], 1);
+#pragma unroll
+  for (int r = 0; r < kPer; r++)
+    if (tid + 1024 * r < n) atomicAdd(&cnt[dgs[r]], 1);
   __syncthreads();
   // exclusive scan of the 256 digit counts by the first 4 waves
   if (tid < 256) {
@@ -262,17 +273,25 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
     int32_t pre = 0;
     for (int ww = 0; ww < w; ww++) pre += wsum[ww];
     run[tid] = cnt[tid] + pre;
-    if (tid < E) offsets[tid] = run[tid];
+    if (tid < E) {
+      offsets[tid] = run[tid];
+      off[tid] = run[tid];
+    }
   }
-  if (tid == 0) offsets[E] = (int32_t)n;
+  if (tid == 0) {
+    offsets[E] = (int32_t)n;
+    off[E] = (int32_t)n;
+  }
   __syncthreads();
   for (int e = tid; e < E; e += 1024)
     counts[e] = (e + 1 < E ? run[e + 1] : (int32_t)n) - run[e];
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = 0; base < n; base += 1024) {
-    const int64_t i = base + tid;
+#pragma unroll
+  for (int r = 0; r < kPer; r++) {
+    if (1024 * r >= n) break;
+    const int64_t i = tid + 1024 * r;
     const bool valid = i < n;
-    const int dg = valid ? (group_of(idx[i], gk) & mask) : 0;
+    const int dg = dgs[r];
     uint64_t same = __ballot(valid);
     for (int b = 0; b < bits; b++) {
       const uint64_t bb = __ballot(valid && ((dg >> b) & 1));
@@ -300,7 +319,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
     __syncthreads();
   }
   if (tb.tiles)
-    build_tile_list(offsets, tb);
+    build_tile_list(off, tb);
 }
 
 // offsets[e] = first sorted position whose expert is >= e, read off the

@@ -325,28 +325,6 @@ __device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[V], i
   return th;
 }
 
-// Two threshold searches in one bit loop (two independent chains of
-// ballots and counts; each stops at its own exact count).
-template <int V>
-__device__ __forceinline__ void select_threshold2(const uint32_t (&k0)[V], int K0, uint32_t& th0,
-                                                  const uint32_t (&k1)[V], int K1,
-                                                  uint32_t& th1) {
-  th0 = th1 = 0;
-  bool d0 = false, d1 = false;
-  for (int b = 31; b >= 0 && !(d0 && d1); b--) {
-    const uint32_t c0 = th0 | (1u << b), c1 = th1 | (1u << b);
-    const int n0 = count_ge<V>(k0, c0), n1 = count_ge<V>(k1, c1);
-    if (!d0) {
-      if (n0 >= K0) th0 = c0;
-      d0 = n0 == K0;
-    }
-    if (!d1) {
-      if (n1 >= K1) th1 = c1;
-      d1 = n1 == K1;
-    }
-  }
-}
-
 // Marks in sel (bit i = slot i) the K best pairs given the threshold th of
 // select_threshold: every key above th is taken, and the keys equal to th
 // are taken by ascending id until K are.
@@ -482,8 +460,10 @@ __global__ __launch_bounds__(256) void k_select_pk(const float* __restrict__ sco
       id2[side][i] = e;
     }
   }
-  uint32_t th2[2];
-  select_threshold2<V>(key2[0], krow, th2[0], key2[1], kcol, th2[1]);
+  // two plain searches: the scalar unit (shared by the CU's SIMDs) is the
+  // bound here, and one loop per side carries far less loop control than
+  // one loop interleaving both
+  const uint32_t th2[2] = {select_threshold<V>(key2[0], krow), select_threshold<V>(key2[1], kcol)};
 #pragma unroll
   for (int side = 0; side < 2; side++) {
     const uint32_t sel = select_at<V>(key2[side], id2[side], side ? kcol : krow, th2[side]);
