@@ -519,12 +519,16 @@ __device__ __forceinline__ void gemm_tile_ring(const GemmArgs& args, const TileC
     }
   };
 
-  // prologue: copies 0 .. min(20, nk S) - 1 (slots in ring order), tile 0
-  // published, its first step's fragments in registers
+  // prologue: copies 0 .. min(20, nk S) - 1 (slots in ring order, except
+  // that tile 0 issues its weight slots before its gathered rows, whose
+  // addresses wait on the row-index load), tile 0 published, its first
+  // step's fragments in registers
   const int pro = nk * S < NSLOT ? nk * S : NSLOT;
 #pragma unroll
-  for (int q = 0; q < NSLOT; q++)
-    if (q < pro) copy_q(q / S, q % S, q);
+  for (int q = 0; q < NSLOT; q++) {
+    const int j = q < S ? (q < SB ? SA + q : q - SB) : q % S;
+    if (q < pro) copy_q(q / S, j, q < S ? j : q);
+  }
   wait_vmcnt_n(pro - S);
   __builtin_amdgcn_s_barrier();
 #pragma unroll
