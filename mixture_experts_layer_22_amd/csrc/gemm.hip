@@ -101,10 +101,17 @@ __device__ __forceinline__ T* c_row(const GemmArgs& a, const TileCtx<SWIGLU>& c,
 // takes its equal share of them, items [x S/8, (x+1) S/8), so every XCD
 // starts its long items first and no XCD ends on a run of them; then its
 // range, walked from the end when a.rev is set.  Blocks past both exit.
-__device__ __forceinline__ bool work_item(const GemmArgs& a, int& m_tile, int& n_tile) {
+__device__ __forceinline__ bool work_item(const GemmArgs& a, int& m_tile, int& n_tile,
+                                          int& half) {
   const int b = blockIdx.x;
   const int x = b % kXcds;
   int j = b / kXcds;
+  // halves: consecutive blocks of an XCD take the two halves of one item
+  half = 0;
+  if (a.halves_ok && a.xcd_first[kXcds + 1]) {
+    half = 1 + (j & 1);
+    j >>= 1;
+  }
   int w;
   const int s0 = (int)((int64_t)x * a.shared_items / kXcds);
   const int s1 = (int)((int64_t)(x + 1) * a.shared_items / kXcds);
@@ -141,8 +148,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm_bf16(GemmArgs arg
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[BN * BK];
 
-  int tile_id, n_tile;
-  if (!work_item(args, tile_id, n_tile)) return;
+  int tile_id, n_tile, half;
+  if (!work_item(args, tile_id, n_tile, half)) return;
+  (void)half;  // whole items only
   const int4 tl = args.tiles[tile_id];
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl, tile_id - tl.w);
   const int n0 = n_tile * BNO;
@@ -564,8 +572,8 @@ __device__ __forceinline__ void gemm_tile_ring(const GemmArgs& args, const TileC
 template <bool SWIGLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dl(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kGemmLdsElems];
-  int tile_id, n_tile;
-  if (!work_item(args, tile_id, n_tile)) return;
+  int tile_id, n_tile, half;
+  if (!work_item(args, tile_id, n_tile, half)) return;
   // Inside its group the item list is walked N chunk by N chunk: a chunk
   // holds all G M tiles of the group times about 32/G N tiles, at least 4,
   // so the ~32 blocks an XCD runs at once share both their gathered rows and
@@ -585,9 +593,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_dl(GemmArgs args) {
   const int v = u - chunk * G * gw;
   const int g = v / cw;
   n_tile = chunk * gw + (v - g * cw);
-  const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl, g);
+  TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl, g);
   const int n0 = n_tile * (SWIGLU ? 128 : 256);
   if (n0 >= c.N) return;
+  if (half) {  // rows [0, 128) or [128, 256) of the item
+    if (half == 2) {
+      c.r0 += 128;
+      c.nr -= 128;
+    } else if (c.nr > 128) {
+      c.nr = 128;
+    }
+    if (c.nr <= 0) return;
+  }
   if (c.nr > 192)
     gemm_tile_ring<256, SWIGLU>(args, c, n0, lds);
   else if (c.nr > 128)
@@ -609,8 +626,9 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs args) {
   constexpr int NB = SWIGLU ? 128 : 64;   // B rows staged per chunk
   __shared__ float sa[32][KC + 1];
   __shared__ float sb[NB][KC + 1];
-  int tile_id, n_tile;
-  if (!work_item(args, tile_id, n_tile)) return;
+  int tile_id, n_tile, half;
+  if (!work_item(args, tile_id, n_tile, half)) return;
+  (void)half;  // whole items only
   const int4 tl = args.tiles[tile_id];
   const TileCtx<SWIGLU> c = tile_ctx<SWIGLU>(args, tl, tile_id - tl.w);
   const int n0 = n_tile * 64;
@@ -713,7 +731,9 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, int BM, const GemmArgs& a
   if (max_tiles == 0 || Nmax == 0) return hipSuccess;
   a.n_ntiles = gemm_n_ntiles(dtype, swiglu, Nmax);
   a.bm = BM;
-  const unsigned grid = (unsigned)(gemm_blocks_per_xcd(BM, max_tiles, a.n_ntiles) * kXcds);
+  a.halves_ok = (dtype == MOE_BF16 && BM == 256 && !swiglu) ? 1 : 0;
+  const unsigned grid = (unsigned)(gemm_blocks_per_xcd(BM, max_tiles, a.n_ntiles) * kXcds *
+                                   (a.halves_ok ? 2 : 1));
   if (dtype == MOE_F32) {
     if (swiglu)
       hipLaunchKernelGGL(k_grouped_gemm_f32<true>, dim3(grid), dim3(256), 0, st, a);

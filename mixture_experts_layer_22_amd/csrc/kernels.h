@@ -10,7 +10,9 @@ namespace moe {
 // (g = 0: the gated GEMM, 1: the down projection), [1 + 9 g + 8] = number of
 // work items.  A work item is one (M tile, N tile) pair, M-tile major.
 constexpr int kXcds = 8;
-constexpr int kSchedInts = 1 + 2 * (kXcds + 1);
+// schedule: valid tiles, each GEMM's 9 XCD boundaries, then whether the
+// down projection runs its items as two 128-row halves
+constexpr int kSchedInts = 1 + 2 * (kXcds + 1) + 1;
 
 struct GemmArgs {
   const int4* tiles;         // per M tile: {group, group's first row, group's rows, group's first tile}
@@ -52,6 +54,10 @@ struct GemmArgs {
   int shared_items;
   int n_ntiles;            // N tiles per M tile (set by the launcher)
   int bm;                  // rows per M tile (set by the launcher)
+  // 256-row down projection: the tile builder may have it run every item as
+  // two 128-row halves (its schedule entry after the XCD boundaries), for
+  // which the launcher provides two blocks per item
+  int halves_ok;
 };
 
 // Element offset of K column kcol of a shared-group B row, beyond kcol

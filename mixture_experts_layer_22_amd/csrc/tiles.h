@@ -153,6 +153,18 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
     for (int x = kXcds - 1; x >= 1; x--) b[x] = max(b[x], b[x + 1] - cap);
 #pragma unroll 1
     for (int x = 0; x <= kXcds; x++) tb.sched[1 + e * (kXcds + 1) + x] = b[x];
+    if (e == 1) {
+      // the down projection as 128-row halves: an XCD runs one 256-row item
+      // per CU at a time, so with R items on its 32 CUs it takes ceil(R/32)
+      // rounds, or ceil(2R/32) rounds of halves; a half takes about 0.62 of
+      // an item (measured: the 128-row tile reads 1.5x the bytes per FLOP)
+      int R = 0;
+#pragma unroll 1
+      for (int x = 0; x < kXcds; x++) R = max(R, b[x + 1] - b[x]);
+      R += (n_shared ? per_shared * (int)tb.nn2 + kXcds - 1 : 0) / kXcds;
+      const int r1 = (R + 31) / 32, r2 = (2 * R + 31) / 32;
+      tb.sched[1 + 2 * (kXcds + 1)] = (BM == 256 && 62 * r2 < 95 * r1) ? 1 : 0;
+    }
   }
   if (e == 0) tb.sched[0] = routed_total + n_shared * per_shared;
 }
