@@ -82,12 +82,17 @@ __global__ __launch_bounds__(64 * NW) void k_router_logits_bf16(
 
   // B loader: 64 rows x 16 float4 = 1024 float4, BL per thread; float4 i
   // of this thread is row id/16, K elements 4(id%16) .. +3
+  // Rows past NL load a valid row (unconditional loads) but are neither
+  // split nor stored: their logits are never written, and a router of
+  // fewer than 64 experts skips most of the splitting.
   const float* bsrc[BL];
   int bdst[BL];
+  bool bok[BL];
 #pragma unroll
   for (int i = 0; i < BL; i++) {
     const int id = tid + NT * i;
     const int nl = id >> 4, k4 = (id & 15) * 4;
+    bok[i] = n0 + nl < NL;
     const int n = n0 + nl < NL ? n0 + nl : NL - 1;
     bsrc[i] = W + (int64_t)n * K + kbeg + k4;
     bdst[i] = nl * 64 + (((k4 >> 3) ^ rl_swz(nl)) * 8) + (k4 & 7);  // slice 0 position
@@ -100,6 +105,7 @@ __global__ __launch_bounds__(64 * NW) void k_router_logits_bf16(
   auto bstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < BL; i++) {
+      if (!bok[i]) continue;
       uint16_t h[4], m[4], l[4];
 #pragma unroll
       for (int e = 0; e < 4; e++) split3(breg[i][e], h[e], m[e], l[e]);
