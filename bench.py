@@ -385,13 +385,20 @@ def main():
     from mixture_experts_layer_22_amd import inputs as I
 
     if args.calibrate_copy:
+        # counter calibration: a device copy of COPY_BYTES (plain loads and
+        # stores), then the same bytes streamed once through plain loads and
+        # once through direct-to-LDS loads (the expert GEMM's load kind)
         n = COPY_BYTES // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
+        sums = torch.empty(1024, dtype=torch.float32, device="cuda:0")
+        B.moe_probe_stream_read(src, n, sums, 1024)
+        B.moe_probe_stream_read_lds(src, n, sums, 1024)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3,
+                          "stream_reads": ["k_stream_read", "k_stream_read_lds"]}))
         return
 
     if args.tau_sweep:

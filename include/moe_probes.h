@@ -24,6 +24,19 @@ extern "C" {
 int32_t moe_probe_stream_read(const float* buf, int64_t n, float* block_sums, int blocks,
                               moe_stream stream);
 
+/* The same read through direct-to-LDS loads (global_load_lds, the expert
+ * GEMM's load kind): block b streams floats [b n/blocks, (b+1) n/blocks),
+ * 4 KB per step, and sums what landed in LDS; the counter calibration of
+ * the traffic records runs it beside a plain copy.
+ *
+ * buf: device, n floats, 16-byte aligned; n a multiple of 4096 * blocks.
+ * block_sums: device, `blocks` floats, written.  blocks in [1, 65536].
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE; nothing is written on error.
+ *   Asynchronous on `stream`; allocates nothing.
+ */
+int32_t moe_probe_stream_read_lds(const float* buf, int64_t n, float* block_sums, int blocks,
+                                  moe_stream stream);
+
 /* Row gather: n_idx / per_wave waves; wave w reads the table rows
  * idx[w*per_wave .. (w+1)*per_wave) whole (row_bytes each, 16-byte loads,
  * 8 rows in flight) and sums them as fp32: the access pattern of a token

@@ -280,7 +280,8 @@ def moe_ablation_atomic_token_centric(dims, w: DeviceWeights, x, T, topk_idx, to
 # ---------------------------------------------------------------- ceiling probes
 
 PRB_PATH = os.path.join(HERE, "libmoe_probes.so")
-PRB_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_loop", "moe_probe_row_gather"]
+PRB_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_loop", "moe_probe_row_gather",
+                "moe_probe_stream_read_lds"]
 _prb = None
 
 
@@ -297,6 +298,8 @@ def load_probes(path: str = PRB_PATH) -> ctypes.CDLL:
     P = ctypes.c_void_p
     lib.moe_probe_stream_read.restype = ctypes.c_int32
     lib.moe_probe_stream_read.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
+    lib.moe_probe_stream_read_lds.restype = ctypes.c_int32
+    lib.moe_probe_stream_read_lds.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
     lib.moe_probe_row_gather.restype = ctypes.c_int32
     lib.moe_probe_row_gather.argtypes = [P, ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64,
                                          ctypes.c_int, P, P]
@@ -309,6 +312,12 @@ def load_probes(path: str = PRB_PATH) -> ctypes.CDLL:
 def moe_probe_stream_read(buf, n, block_sums, blocks, stream=None):
     _check(load_probes().moe_probe_stream_read(_ptr(buf), int(n), _ptr(block_sums), int(blocks),
                                                _stream(stream)), "moe_probe_stream_read")
+
+
+def moe_probe_stream_read_lds(buf, n, block_sums, blocks, stream=None):
+    _check(load_probes().moe_probe_stream_read_lds(_ptr(buf), int(n), _ptr(block_sums),
+                                                   int(blocks), _stream(stream)),
+           "moe_probe_stream_read_lds")
 
 
 def moe_probe_row_gather(table, n_rows, row_bytes, idx, n_idx, per_wave, wave_sums,

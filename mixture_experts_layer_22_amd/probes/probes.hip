@@ -37,6 +37,41 @@ __global__ __launch_bounds__(256) void k_stream_read(const f32x4* __restrict__ b
   if (threadIdx.x == 0) block_sums[blockIdx.x] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
 }
 
+// The same streaming read through direct-to-LDS loads (global_load_lds,
+// the expert GEMM's load kind): each block streams its contiguous share,
+// 4 KB per step (lane l's 16 bytes land at LDS offset 16 l of its wave's
+// 1 KB), 4 steps in flight; every thread then reads its own 16 bytes back
+// from LDS and sums them, so the sums show every element was read.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+__global__ __launch_bounds__(256) void k_stream_read_lds(const f32x4* __restrict__ buf,
+                                                         int64_t per_block,
+                                                         float* __restrict__ block_sums) {
+  __shared__ __attribute__((aligned(16))) f32x4 lds[4 * 256];
+  __shared__ float ws[4];
+  const f32x4* base = buf + (int64_t)blockIdx.x * per_block;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  float s = 0.f;
+  for (int64_t off = 0; off < per_block; off += 4 * 256) {
+#pragma unroll
+    for (int st = 0; st < 4; st++)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + off + st * 256 + tid),
+                                       (lds_void_t*)(lds + st * 256 + wave * 64), 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+      const f32x4 a = lds[st * 256 + tid];
+      s += (a[0] + a[1]) + (a[2] + a[3]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads done before the next copies
+  }
+  s = wave_sum(s);
+  if ((tid & 63) == 0) ws[wave] = s;
+  __syncthreads();
+  if (tid == 0) block_sums[blockIdx.x] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+}
+
 // Row gather: wave w reads the rows idx[w*per .. w*per + per) of a table
 // of 16-byte units (U units per lane and row: lane l takes units l, l+64,
 // ...), 8 rows in flight at a time, and sums them; one partial per wave.
@@ -107,6 +142,18 @@ extern "C" int32_t moe_probe_stream_read(const float* buf, int64_t n, float* blo
     return MOE_ERR_SHAPE;
   hipLaunchKernelGGL(k_stream_read, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      reinterpret_cast<const f32x4*>(buf), n / 4, block_sums);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" int32_t moe_probe_stream_read_lds(const float* buf, int64_t n, float* block_sums,
+                                             int blocks, moe_stream stream) {
+  using namespace moe_probes;
+  if (!buf || !block_sums) return MOE_ERR_NULL;
+  if (n < 0 || blocks < 1 || blocks > 65536 || (uintptr_t)buf % 16 != 0 ||
+      n % ((int64_t)blocks * 4096) != 0)
+    return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(k_stream_read_lds, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     reinterpret_cast<const f32x4*>(buf), n / 4 / blocks, block_sums);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

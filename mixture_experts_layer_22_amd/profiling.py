@@ -99,6 +99,15 @@ def traffic_record(kernel, copy_fetch, copy_write, fetch, write, copy_bytes, cop
     w, nw = counter_per_dispatch(write, "WRITE_SIZE", kernel)
     fetch_scale = copy_bytes / (cf * 1024.0)
     write_scale = copy_bytes / (cw * 1024.0)
+    # the calibration run also streams copy_bytes once through plain loads
+    # and once through direct-to-LDS loads: their FETCH_SIZE shows whether
+    # the copy's factor holds for both load kinds
+    reads = {}
+    for k in ("k_stream_read(", "k_stream_read_lds"):
+        try:
+            reads[k.rstrip("(")] = counter_per_dispatch(copy_fetch, "FETCH_SIZE", k, "max")[0]
+        except (ValueError, FileNotFoundError):
+            pass
     return {
         "kernel": kernel,
         "fetch_bytes": f * 1024.0 * fetch_scale,
@@ -107,6 +116,7 @@ def traffic_record(kernel, copy_fetch, copy_write, fetch, write, copy_bytes, cop
         "fetch_kib_raw": f, "write_kib_raw": w,
         "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": copy_bytes,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "calibration_stream_reads_fetch_kib": reads,
         "dispatches": [nf, nw],
         "source": kernel_source(kernel),
         "source_sha256": kernel_source_sha(kernel),

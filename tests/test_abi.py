@@ -273,6 +273,13 @@ def test_probes_reject_on_host(prb):
     assert mfma(0, P, 4, None) == B.MOE_ERR_SHAPE
     assert mfma((1 << 19) + 1, P, 4, None) == B.MOE_ERR_SHAPE
     assert mfma(10, P, 0, None) == B.MOE_ERR_SHAPE
+    rl = prb.moe_probe_stream_read_lds
+    assert rl(None, 4096, P, 1, None) == B.MOE_ERR_NULL
+    assert rl(P, 4096, None, 1, None) == B.MOE_ERR_NULL
+    assert rl(P, 4096 + 4, P, 1, None) == B.MOE_ERR_SHAPE    # not whole 16 KB steps per block
+    assert rl(P, 4096, P, 2, None) == B.MOE_ERR_SHAPE        # 2048 floats per block
+    assert rl(P + 4, 4096, P, 1, None) == B.MOE_ERR_SHAPE    # misaligned
+    assert rl(P, 4096, P, 0, None) == B.MOE_ERR_SHAPE
     gather = prb.moe_probe_row_gather
     assert gather(None, 8, 2048, P, 32, 32, P, None) == B.MOE_ERR_NULL
     assert gather(P, 8, 2048, None, 32, 32, P, None) == B.MOE_ERR_NULL
