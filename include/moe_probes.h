@@ -24,6 +24,19 @@ extern "C" {
 int32_t moe_probe_stream_read(const float* buf, int64_t n, float* block_sums, int blocks,
                               moe_stream stream);
 
+/* Block-contiguous streaming read: block b sums floats
+ * [b n/blocks, (b+1) n/blocks) with 16-byte loads, 32 KB per step (512
+ * threads, four loads each).  Concurrent reads fall in `blocks` separate
+ * regions instead of one window moving over the buffer.
+ *
+ * buf: device, n floats, 16-byte aligned; n a multiple of 8192 * blocks.
+ * block_sums: device, `blocks` floats, written.  blocks in [1, 65536].
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE; nothing is written on error.
+ *   Asynchronous on `stream`; allocates nothing.
+ */
+int32_t moe_probe_stream_read_blocks(const float* buf, int64_t n, float* block_sums, int blocks,
+                                     moe_stream stream);
+
 /* The same read through direct-to-LDS loads (global_load_lds, the expert
  * GEMM's load kind): block b streams floats [b n/blocks, (b+1) n/blocks),
  * 4 KB per step, and sums what landed in LDS; the counter calibration of

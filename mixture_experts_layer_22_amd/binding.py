@@ -281,7 +281,7 @@ def moe_ablation_atomic_token_centric(dims, w: DeviceWeights, x, T, topk_idx, to
 
 PRB_PATH = os.path.join(HERE, "libmoe_probes.so")
 PRB_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_loop", "moe_probe_row_gather",
-                "moe_probe_stream_read_lds"]
+                "moe_probe_stream_read_lds", "moe_probe_stream_read_blocks"]
 _prb = None
 
 
@@ -298,6 +298,8 @@ def load_probes(path: str = PRB_PATH) -> ctypes.CDLL:
     P = ctypes.c_void_p
     lib.moe_probe_stream_read.restype = ctypes.c_int32
     lib.moe_probe_stream_read.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
+    lib.moe_probe_stream_read_blocks.restype = ctypes.c_int32
+    lib.moe_probe_stream_read_blocks.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
     lib.moe_probe_stream_read_lds.restype = ctypes.c_int32
     lib.moe_probe_stream_read_lds.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
     lib.moe_probe_row_gather.restype = ctypes.c_int32
@@ -312,6 +314,12 @@ def load_probes(path: str = PRB_PATH) -> ctypes.CDLL:
 def moe_probe_stream_read(buf, n, block_sums, blocks, stream=None):
     _check(load_probes().moe_probe_stream_read(_ptr(buf), int(n), _ptr(block_sums), int(blocks),
                                                _stream(stream)), "moe_probe_stream_read")
+
+
+def moe_probe_stream_read_blocks(buf, n, block_sums, blocks, stream=None):
+    _check(load_probes().moe_probe_stream_read_blocks(_ptr(buf), int(n), _ptr(block_sums),
+                                                      int(blocks), _stream(stream)),
+           "moe_probe_stream_read_blocks")
 
 
 def moe_probe_stream_read_lds(buf, n, block_sums, blocks, stream=None):

@@ -1,5 +1,5 @@
-// Ceiling probes (libmoe_probes.so): a streaming read, a row gather and a
-// memory-free MFMA loop, the measured rates the layer's kernels are set
+// Ceiling probes (libmoe_probes.so): streaming reads (grid-stride,
+// block-contiguous, direct-to-LDS), a row gather and a memory-free MFMA loop, the measured rates the layer's kernels are set
 // against beside the datasheet peaks.  Only the benchmark and its tests
 // call them.
 #include "../../include/moe_probes.h"
@@ -35,6 +35,32 @@ __global__ __launch_bounds__(256) void k_stream_read(const f32x4* __restrict__ b
   if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
   __syncthreads();
   if (threadIdx.x == 0) block_sums[blockIdx.x] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+}
+
+// Block-contiguous streaming read: block b reads its own contiguous share
+// [b n/blocks, (b+1) n/blocks) in 32 KB steps (512 threads, four 16-byte
+// loads each, issued together), so that concurrent reads fall in `blocks`
+// separate regions rather than in one window moving over the buffer.
+__global__ __launch_bounds__(512) void k_stream_read_blocks(const f32x4* __restrict__ buf,
+                                                            int64_t per_block,
+                                                            float* __restrict__ block_sums) {
+  __shared__ float ws[8];
+  const f32x4* base = buf + (int64_t)blockIdx.x * per_block;
+  const int tid = threadIdx.x;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  for (int64_t off = 0; off < per_block; off += 2048) {
+    const f32x4 a = base[off + tid], b = base[off + 512 + tid], c = base[off + 1024 + tid],
+                d = base[off + 1536 + tid];
+    s0 += (a[0] + a[1]) + (a[2] + a[3]);
+    s1 += (b[0] + b[1]) + (b[2] + b[3]);
+    s2 += (c[0] + c[1]) + (c[2] + c[3]);
+    s3 += (d[0] + d[1]) + (d[2] + d[3]);
+  }
+  const float s = wave_sum((s0 + s1) + (s2 + s3));
+  if ((tid & 63) == 0) ws[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0)
+    block_sums[blockIdx.x] = ((ws[0] + ws[1]) + (ws[2] + ws[3])) + ((ws[4] + ws[5]) + (ws[6] + ws[7]));
 }
 
 // The same streaming read through direct-to-LDS loads (global_load_lds,
@@ -142,6 +168,19 @@ extern "C" int32_t moe_probe_stream_read(const float* buf, int64_t n, float* blo
     return MOE_ERR_SHAPE;
   hipLaunchKernelGGL(k_stream_read, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      reinterpret_cast<const f32x4*>(buf), n / 4, block_sums);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" int32_t moe_probe_stream_read_blocks(const float* buf, int64_t n, float* block_sums,
+                                                int blocks, moe_stream stream) {
+  using namespace moe_probes;
+  if (!buf || !block_sums) return MOE_ERR_NULL;
+  if (n < 0 || blocks < 1 || blocks > 65536 || (uintptr_t)buf % 16 != 0 ||
+      n % ((int64_t)blocks * 8192) != 0)
+    return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(k_stream_read_blocks, dim3((unsigned)blocks), dim3(512), 0,
+                     (hipStream_t)stream, reinterpret_cast<const f32x4*>(buf), n / 4 / blocks,
+                     block_sums);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -280,6 +280,13 @@ def test_probes_reject_on_host(prb):
     assert rl(P, 4096, P, 2, None) == B.MOE_ERR_SHAPE        # 2048 floats per block
     assert rl(P + 4, 4096, P, 1, None) == B.MOE_ERR_SHAPE    # misaligned
     assert rl(P, 4096, P, 0, None) == B.MOE_ERR_SHAPE
+    rb = prb.moe_probe_stream_read_blocks
+    assert rb(None, 8192, P, 1, None) == B.MOE_ERR_NULL
+    assert rb(P, 8192, None, 1, None) == B.MOE_ERR_NULL
+    assert rb(P, 8192 + 4, P, 1, None) == B.MOE_ERR_SHAPE    # not whole 32 KB steps per block
+    assert rb(P, 8192, P, 2, None) == B.MOE_ERR_SHAPE        # 4096 floats per block
+    assert rb(P + 4, 8192, P, 1, None) == B.MOE_ERR_SHAPE    # misaligned
+    assert rb(P, 8192, P, 0, None) == B.MOE_ERR_SHAPE
     gather = prb.moe_probe_row_gather
     assert gather(None, 8, 2048, P, 32, 32, P, None) == B.MOE_ERR_NULL
     assert gather(P, 8, 2048, None, 32, 32, P, None) == B.MOE_ERR_NULL
