@@ -204,6 +204,70 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   }
 }
 
+// Small batches: one wave per (token, 512-element column slice), so a
+// decode batch of 16 tokens runs 64 waves instead of 16 and every slot's row
+// slice is loaded at once (up to 8 rows in flight per lane): the metadata
+// and one round of row loads instead of one round per two slots.  Each
+// output element takes the same additions in the same order as in
+// k_combine, so both give identical results.  No constant experts (their
+// coefficients need the whole row).
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine_cols(CombineArgs a, int slices) {
+  constexpr int CH = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = w / slices;
+  if (t >= a.T) return;
+  const int d = a.d, nu = d / 8, k = a.k;
+  const int u = (int)(w - t * slices) * 64 + lane;
+  const bool on = u < nu;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) acc[q] = 0.f;
+  int me = 0, mp = 0;
+  float mg = 0.f;
+  if (lane < k) {
+    me = a.idx[t * k + lane];
+    mg = a.gate[t * k + lane];
+    mp = a.inv_perm[t * k + lane];
+  }
+  const T* sy = reinterpret_cast<const T*>(a.shared_y);
+  for (int s = 0; s < a.n_shared; s++) {
+    if (on) {
+      Raw8<T> r;
+      r.load(sy + ((int64_t)s * a.T + t) * d + u * 8);
+#pragma unroll
+      for (int q = 0; q < 8; q++) acc[q] += r[q];
+    }
+  }
+  const T* xrow = reinterpret_cast<const T*>(a.x) + t * d;
+  const T* y = reinterpret_cast<const T*>(a.y);
+  for (int j0 = 0; j0 < k; j0 += CH) {
+    Raw8<T> r[CH];
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+      const int j = j0 + c;
+      if (j < k && on) {
+        const int e = readlane_i(me, j);
+        if (e < a.E_ffn) r[c].load(y + (int64_t)readlane_i(mp, j) * d + u * 8);
+        else if (a.zc_kind[e - a.E_ffn] == MOE_ZC_COPY) r[c].load(xrow + u * 8);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+      const int j = j0 + c;
+      if (j >= k) break;
+      const int e = readlane_i(me, j);
+      const float g = readlane_f(mg, j);
+      if (e >= a.E_ffn && a.zc_kind[e - a.E_ffn] == MOE_ZC_ZERO) continue;
+      if (on)
+#pragma unroll
+        for (int q = 0; q < 8; q++) acc[q] += g * r[c][q];
+    }
+  }
+  if (on) Elt<T>::store8(reinterpret_cast<T*>(a.out) + t * d + u * 8, acc);
+}
+
 // ------------------------------------------------------------------------
 // Atomic stage 1: h[p] = silu(u_e . x_t) for sorted task p (task perm[p] =
 // t*k + j, e = idx[task]).  A wave takes 8 consecutive sorted tasks, 8
@@ -334,9 +398,19 @@ __global__ __launch_bounds__(256) void k_atomic_combine(const T* __restrict__ at
 // ------------------------------------------------------------------------
 // launchers (U = units of 8 elements per lane = ceil(d / 512), d <= 8192)
 
+// batches of at most this many tokens use the column-slice kernel
+constexpr int64_t kCombineColsTokens = 256;
+
 template <typename T>
 static hipError_t combine_t(const CombineArgs& a, hipStream_t st) {
   const int U = (int)cdiv(a.d, 512);
+  bool consts = false;
+  for (int z = 0; z < MOE_MAX_ZC; z++) consts |= a.zc_kind[z] == MOE_ZC_CONST;
+  if (a.T <= kCombineColsTokens && !consts) {
+    hipLaunchKernelGGL(k_combine_cols<T>, dim3((unsigned)cdiv(a.T * U, 4)), dim3(256), 0, st, a,
+                       U);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)cdiv(a.T, 4)), block(256);
   if (U <= 1) hipLaunchKernelGGL((k_combine<T, 1>), grid, block, 0, st, a);
   else if (U <= 2) hipLaunchKernelGGL((k_combine<T, 2>), grid, block, 0, st, a);
