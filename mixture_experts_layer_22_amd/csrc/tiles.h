@@ -38,12 +38,13 @@ __device__ __forceinline__ int tile_base(int BM, int g) { return BM == 256 ? 3 +
 // Tiles [first, first + n) of one group, all of `full` rows but the last of
 // `last` rows, starting at cost prefix P[g] in GEMM g with cost weight w[g]
 // (1, or 0: not in that GEMM's ranges): writes every XCD boundary that falls
-// in them into bnd[g].  A target t lands in tile i (prefix Pi, cost c) when Pi*nn < t <=
-// (Pi+c)*nn, at item i*nn + ceil((t - Pi*nn) / c).
+// in them into bnd[g].  The boundaries' targets tgt[g][x] = ceil(x total_g
+// nn_g / 8) are in LDS.  A target t lands in tile i (prefix Pi, cost c) when
+// Pi*nn < t <= (Pi+c)*nn, at item i*nn + ceil((t - Pi*nn) / c).
 __device__ __forceinline__ void place_targets(int first, int n, int full, int last, int BM,
-                                              const int64_t (&P)[2], const int64_t (&total)[2],
-                                              const int (&w)[2], int nn1, int nn2,
-                                              int32_t (*bnd)[kXcds + 1]) {
+                                              const int64_t (&P)[2],
+                                              const int64_t (*tgts)[kXcds], const int (&w)[2],
+                                              int nn1, int nn2, int32_t (*bnd)[kXcds + 1]) {
   // rolled loops: the kernel runs once per layer call on a cold instruction
   // cache, so its code must stay small; offsets inside one group fit in 32
   // bits, so the divisions are 32-bit
@@ -56,7 +57,7 @@ __device__ __forceinline__ void place_targets(int first, int n, int full, int la
     const int64_t lo = P[g] * nn, hi = (P[g] + (int64_t)(n - 1) * cf + cl) * nn;
 #pragma unroll 1
     for (int x = 1; x < kXcds; x++) {
-      const int64_t tgt = (x * total[g] * nn + kXcds - 1) / kXcds;
+      const int64_t tgt = tgts[g][x];
       if (tgt <= lo || tgt > hi) continue;
       // full tiles first, then the last one
       const uint32_t d = (uint32_t)(tgt - lo);  // in [1, hi - lo]
@@ -75,6 +76,7 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
                                                 const TileBuild& tb) {
   __shared__ int32_t wtot[2][16];
   __shared__ int32_t bnd[2][kXcds + 1];
+  __shared__ int64_t tgts[2][kXcds];
   const int E_ffn = tb.E_ffn, n_shared = tb.n_shared, BM = tb.BM;
   const int64_t T = tb.T;
   const int e = threadIdx.x, nthreads = blockDim.x, nwaves = nthreads >> 6;
@@ -94,14 +96,16 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   if (lane == 63) { wtot[0][wv] = sn; wtot[1][wv] = sc; }
   if (e < 2 * (kXcds + 1)) bnd[e / (kXcds + 1)][e % (kXcds + 1)] = 0;  // targets of an empty list
   __syncthreads();
-  int bn = 0, bc = 0, tn = 0, tc = 0;
-#pragma unroll 1
-  for (int w = 0; w < nwaves; w++) {
-    const int a = wtot[0][w], b = wtot[1][w];
-    if (w < wv) { bn += a; bc += b; }
-    tn += a;
-    tc += b;
+  // the waves' totals, one per lane: inclusive scan, then the lanes before
+  // this wave's and the last
+  int qn = lane < nwaves ? wtot[0][lane] : 0, qc = lane < nwaves ? wtot[1][lane] : 0;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const int a = __shfl_up(qn, o, 64), b = __shfl_up(qc, o, 64);
+    if (lane >= o) { qn += a; qc += b; }
   }
+  const int bn = wv ? __shfl(qn, wv - 1, 64) : 0, bc = wv ? __shfl(qc, wv - 1, 64) : 0;
+  const int tn = __shfl(qn, nwaves - 1, 64), tc = __shfl(qc, nwaves - 1, 64);
   const int start = bn + sn - nt;              // exclusive prefix of tile counts
   const int cstart = bc + sc - ce;             // exclusive prefix of tile row units
   const int routed_total = tn;
@@ -127,17 +131,21 @@ __device__ __forceinline__ void build_tile_list(const int32_t* __restrict__ offs
   const int items[2] = {(routed_total + n_shared * per_shared) * tb.nn1,
                         routed_total * tb.nn2};
   if (e < 2) bnd[e][kXcds] = items[e];
+  if (e < 2 * kXcds) {
+    const int g = e / kXcds, x = e % kXcds;
+    tgts[g][x] = (x * total[g] * (g == 0 ? tb.nn1 : tb.nn2) + kXcds - 1) / kXcds;
+  }
   __syncthreads();
   if (e < E_ffn && nt > 0) {
     const int64_t P[2] = {cstart + (int64_t)tile_base(BM, 0) * start,
                           cstart + (int64_t)tile_base(BM, 1) * start};
     const int w[2] = {1, 1};
-    place_targets(start, nt, BM, last, BM, P, total, w, tb.nn1, tb.nn2, bnd);
+    place_targets(start, nt, BM, last, BM, P, tgts, w, tb.nn1, tb.nn2, bnd);
   }
   if (e < n_shared && per_shared > 0) {
     const int64_t P[2] = {routed_cost[0] + e * cs[0], 0};
     const int w[2] = {1, 0};
-    place_targets(routed_total + e * per_shared, per_shared, BM, shared_last, BM, P, total, w,
+    place_targets(routed_total + e * per_shared, per_shared, BM, shared_last, BM, P, tgts, w,
                   tb.nn1, tb.nn2, bnd);
   }
   __syncthreads();
