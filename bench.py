@@ -520,6 +520,18 @@ def main():
         mf_iters, mf_out, mf_blocks, stream)) * 1e-3) / 1e12
     del mf_out
 
+    # the expert GEMM's K-slice mix alone (one 8-wave block per CU): its
+    # MFMAs, + the fragment reads from LDS, + the direct-to-LDS copies of
+    # the next K tile from an L2-resident 2 MiB source
+    sl_iters, sl_blocks, sl_rows = 2000, 256, 16384
+    sl_src = torch.ones(sl_rows * 64, dtype=torch.bfloat16, device=dev)
+    sl_out = torch.empty(sl_blocks, dtype=torch.float32, device=dev)
+    sl_flop = 2.0 * 16 * 16 * 32 * 64 * 8 * sl_iters * sl_blocks
+    slice_tflops = {name: sl_flop / (best_ms(lambda m=m: B.moe_probe_gemm_slice(
+        m, sl_src, sl_rows, sl_iters, sl_out, sl_blocks, stream)) * 1e-3) / 1e12
+        for m, name in ((0, "mfma"), (1, "lds_reads"), (2, "lds_reads_copies"))}
+    del sl_src, sl_out
+
     work = algorithmic_work(cfg, counts)
     tokens_per_s = T / (ms_per_step * 1e-3)
     roof, stages = rooflines(cfg, work, phase_us, phase_cold_us)
@@ -527,8 +539,12 @@ def main():
     # nothing else runs
     ceiling = {"hbm_read_gbs": read_gbs, "hbm_read_grid_stride_gbs": read_grid_gbs,
                "hbm_read_blocks_gbs": read_blocks_gbs, "mfma_bf16_tflops": mfma_tflops,
+               "gemm_slice_tflops": slice_tflops,
                "frac_of_measured": roof["achieved"] / (read_gbs if roof["unit"] == "GB/s"
                                                        else mfma_tflops)}
+    if roof["unit"] == "TFLOP/s":
+        # against the same K-slice mix with its operands in L2
+        ceiling["frac_of_gemm_slice"] = roof["achieved"] / slice_tflops["lds_reads_copies"]
     if gather_gbs is not None:
         # the combine's requested bytes (T k rows) against the same rows
         # gathered by the probe

@@ -80,6 +80,25 @@ int32_t moe_probe_row_gather(const void* table, int64_t n_rows, int row_bytes,
  */
 int32_t moe_probe_mfma_loop(int64_t iters, float* out, int blocks, moe_stream stream);
 
+/* The expert GEMM's K-slice work alone, at its shape: `blocks` blocks of 8
+ * waves, each wave a 128 x 64 tile of v_mfma_f32_16x16x32_bf16 (64 per wave
+ * per 64-wide K tile), `iters` K tiles, one barrier per K tile.
+ *   mode 0: the MFMAs only (fragments read from LDS once);
+ *   mode 1: + every fragment read from LDS at every 32-wide K step;
+ *   mode 2: + the next K tile's 64 KB copied into LDS with direct-to-LDS
+ *           loads from src (src_rows rows of 128 bytes, re-read by every
+ *           block: keep it a few MB, so that it stays in L2).
+ * 2*16*16*32 * 64 * 8 * iters * blocks FLOP.
+ *
+ * src: device, src_rows * 128 bytes, 16-byte aligned, src_rows >= 512 (mode
+ *   2 only; ignored otherwise).  out: device, `blocks` floats, written.
+ *   iters in [1, 2^20], blocks in [1, 65536].
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE; nothing is written on error.
+ *   Asynchronous on `stream`; allocates nothing.
+ */
+int32_t moe_probe_gemm_slice(int mode, const void* src, int src_rows, int iters, float* out,
+                             int blocks, moe_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -281,7 +281,7 @@ def moe_ablation_atomic_token_centric(dims, w: DeviceWeights, x, T, topk_idx, to
 
 PRB_PATH = os.path.join(HERE, "libmoe_probes.so")
 PRB_EXPORTED = ["moe_probe_stream_read", "moe_probe_mfma_loop", "moe_probe_row_gather",
-                "moe_probe_stream_read_lds", "moe_probe_stream_read_blocks"]
+                "moe_probe_stream_read_lds", "moe_probe_stream_read_blocks", "moe_probe_gemm_slice"]
 _prb = None
 
 
@@ -305,6 +305,9 @@ def load_probes(path: str = PRB_PATH) -> ctypes.CDLL:
     lib.moe_probe_row_gather.restype = ctypes.c_int32
     lib.moe_probe_row_gather.argtypes = [P, ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64,
                                          ctypes.c_int, P, P]
+    lib.moe_probe_gemm_slice.restype = ctypes.c_int32
+    lib.moe_probe_gemm_slice.argtypes = [ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P,
+                                         ctypes.c_int, P]
     lib.moe_probe_mfma_loop.restype = ctypes.c_int32
     lib.moe_probe_mfma_loop.argtypes = [ctypes.c_int64, P, ctypes.c_int, P]
     _prb = lib
@@ -334,6 +337,12 @@ def moe_probe_row_gather(table, n_rows, row_bytes, idx, n_idx, per_wave, wave_su
                                               _ptr(idx), int(n_idx), int(per_wave),
                                               _ptr(wave_sums), _stream(stream)),
            "moe_probe_row_gather")
+
+
+def moe_probe_gemm_slice(mode, src, src_rows, iters, out, blocks, stream=None):
+    _check(load_probes().moe_probe_gemm_slice(int(mode), _ptr(src), int(src_rows), int(iters),
+                                              _ptr(out), int(blocks), _stream(stream)),
+           "moe_probe_gemm_slice")
 
 
 def moe_probe_mfma_loop(iters, out, blocks, stream=None):

@@ -1,5 +1,6 @@
 // Ceiling probes (libmoe_probes.so): streaming reads (grid-stride,
-// block-contiguous, direct-to-LDS), a row gather and a memory-free MFMA loop, the measured rates the layer's kernels are set
+// block-contiguous, direct-to-LDS), a row gather, a memory-free MFMA loop
+// and the expert GEMM's K-slice mix, the measured rates the layer's kernels are set
 // against beside the datasheet peaks.  Only the benchmark and its tests
 // call them.
 #include "../../include/moe_probes.h"
@@ -8,6 +9,7 @@
 namespace moe_probes {
 
 using moe::f32x4;
+using moe::u32x4;
 using moe::wave_sum;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -136,6 +138,79 @@ __global__ __launch_bounds__(256) void k_row_gather(const f32x4* __restrict__ ta
   if (lane == 0) wave_sums[w] = s;
 }
 
+// The expert GEMM's K-slice work alone, at its shape: a 512-thread block of
+// 8 waves (two per SIMD), each wave a 128 x 64 tile of 16x16x32 bf16 MFMAs
+// (128 fp32 accumulators), 64-wide K tiles of A (256 rows) and B (256 rows)
+// in LDS, 128 bytes per row, 16-byte chunks swizzled as in the GEMM, one
+// barrier per K tile.  MODE 0: the MFMAs only, on fragments read once;
+// MODE 1: + every fragment read from LDS at every 32-wide K step (12
+// ds_read_b128 per wave per step); MODE 2: + the next K tile's 64 KB copied
+// into the other of two LDS buffers with direct-to-LDS loads (8 per thread
+// per K tile) from `src`, src_rows rows of 128 bytes that every block
+// re-reads (a few MB: they stay in L2).  64 MFMAs per wave per K tile.
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void k_gemm_slice(const uint16_t* __restrict__ src,
+                                                       int src_rows, int iters,
+                                                       float* __restrict__ out) {
+  constexpr int ROWS = 512, BK = 64;  // A rows 0..255, B rows 256..511
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][ROWS * BK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3, frow = lane & 15;
+  for (int i = tid; i < 2 * ROWS * BK / 8; i += 512)
+    reinterpret_cast<u32x4*>(&lds[0][0])[i] = u32x4{0x3f803f80u, 0x3f803f80u, 0u, 0u};
+  __syncthreads();
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = f32x4{};
+  bf16x8 afr[8], bfr[4];
+  auto frag = [&](int buf, int row, int ks) {
+    const int ch = ((ks * 4 + (lane >> 4)) ^ ((row >> 1) & 7)) * 8;
+    return *reinterpret_cast<const bf16x8*>(&lds[buf][row * BK + ch]);
+  };
+  auto read_frags = [&](int buf, int ks) {
+#pragma unroll
+    for (int fm = 0; fm < 8; fm++) afr[fm] = frag(buf, wm * 128 + fm * 16 + frow, ks);
+#pragma unroll
+    for (int fn = 0; fn < 4; fn++) bfr[fn] = frag(buf, 256 + wn * 64 + fn * 16 + frow, ks);
+  };
+  if (MODE == 0) read_frags(0, 0);
+  for (int it = 0; it < iters; it++) {
+    const int cur = it & 1;
+    if (MODE == 2) {
+      // wave w fills rows 64w .. 64w + 63 of the other buffer, 8 rows per copy
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int r = wave * 64 + 8 * i;
+        const int64_t sr = ((int64_t)(it + 1) * ROWS + r + (lane >> 3)) % src_rows;
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + sr * BK + (lane & 7) * 8),
+                                         (lds_void_t*)&lds[cur ^ 1][r * BK], 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      if (MODE >= 1) read_frags(cur, ks);
+#pragma unroll
+      for (int fm = 0; fm < 8; fm++)
+#pragma unroll
+        for (int fn = 0; fn < 4; fn++)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], afr[fm], acc[fm][fn],
+                                                                0, 0, 0);
+    }
+    if (MODE == 2) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+    __syncthreads();
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) s += (acc[i][j][0] + acc[i][j][1]) + (acc[i][j][2] + acc[i][j][3]);
+  if (s == -1.f) out[blockIdx.x] = s;  // never: keeps every chain live
+  else if (tid == 0) out[blockIdx.x] = acc[0][0][0];
+}
+
 // 16 independent accumulator chains per wave (started at different values
 // so that none can be merged), all-ones operands: each MFMA adds 32 to
 // every element.
@@ -203,6 +278,24 @@ extern "C" int32_t moe_probe_mfma_loop(int64_t iters, float* out, int blocks,
   if (iters < 1 || iters > (1 << 19) || blocks < 1 || blocks > 65536) return MOE_ERR_SHAPE;
   hipLaunchKernelGGL(k_mfma_loop, dim3((unsigned)blocks), dim3(512), 0, (hipStream_t)stream,
                      iters, out);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" int32_t moe_probe_gemm_slice(int mode, const void* src, int src_rows, int iters,
+                                        float* out, int blocks, moe_stream stream) {
+  using namespace moe_probes;
+  if (!out || (mode == 2 && !src)) return MOE_ERR_NULL;
+  if (mode < 0 || mode > 2 || iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536 ||
+      (mode == 2 && (src_rows < 512 || (uintptr_t)src % 16 != 0)))
+    return MOE_ERR_SHAPE;
+  const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+  hipStream_t st = (hipStream_t)stream;
+  if (mode == 0)
+    hipLaunchKernelGGL(k_gemm_slice<0>, dim3((unsigned)blocks), dim3(512), 0, st, s16, src_rows, iters, out);
+  else if (mode == 1)
+    hipLaunchKernelGGL(k_gemm_slice<1>, dim3((unsigned)blocks), dim3(512), 0, st, s16, src_rows, iters, out);
+  else
+    hipLaunchKernelGGL(k_gemm_slice<2>, dim3((unsigned)blocks), dim3(512), 0, st, s16, src_rows, iters, out);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -287,6 +287,14 @@ def test_probes_reject_on_host(prb):
     assert rb(P, 8192, P, 2, None) == B.MOE_ERR_SHAPE        # 4096 floats per block
     assert rb(P + 4, 8192, P, 1, None) == B.MOE_ERR_SHAPE    # misaligned
     assert rb(P, 8192, P, 0, None) == B.MOE_ERR_SHAPE
+    sl = prb.moe_probe_gemm_slice
+    assert sl(0, None, 0, 10, None, 4, None) == B.MOE_ERR_NULL
+    assert sl(2, None, 4096, 10, P, 4, None) == B.MOE_ERR_NULL     # copies need a source
+    assert sl(3, P, 4096, 10, P, 4, None) == B.MOE_ERR_SHAPE       # no such mode
+    assert sl(2, P, 256, 10, P, 4, None) == B.MOE_ERR_SHAPE        # fewer rows than one K tile
+    assert sl(2, P + 4, 4096, 10, P, 4, None) == B.MOE_ERR_SHAPE   # misaligned
+    assert sl(1, None, 0, 0, P, 4, None) == B.MOE_ERR_SHAPE
+    assert sl(1, None, 0, 10, P, 0, None) == B.MOE_ERR_SHAPE
     gather = prb.moe_probe_row_gather
     assert gather(None, 8, 2048, P, 32, 32, P, None) == B.MOE_ERR_NULL
     assert gather(P, 8, 2048, None, 32, 32, P, None) == B.MOE_ERR_NULL

@@ -1,8 +1,8 @@
 """The ceiling probes on the GPU: the streaming read must read every
 element once (its sums are exact on a buffer of ones), the row gather must
 read every listed row whole (its per-wave sums are exact on small integer
-rows), and the MFMA loop must run every MFMA (its accumulators end at
-exactly 32 per round)."""
+rows), and the MFMA loop and the GEMM K-slice probe must run every MFMA
+(their accumulators end at exact multiples of the per-MFMA sum)."""
 import numpy as np
 import pytest
 import torch
@@ -48,6 +48,21 @@ def test_stream_read_blocks_reads_every_element(n, blocks):
     want = [per + 2 * len(range((b * per + 999) // 1000 * 1000, (b + 1) * per, 1000))
             for b in range(blocks)]
     assert np.array_equal(sums.cpu().numpy().astype(np.float64), np.array(want, np.float64))
+
+
+@pytest.mark.parametrize("mode,iters,blocks", [(0, 1, 1), (0, 300, 7), (1, 300, 7), (2, 1, 3),
+                                               (2, 300, 256)])
+def test_gemm_slice_runs_every_mfma(mode, iters, blocks):
+    # every 16-byte LDS chunk starts as bf16 (1, 1, 1, 1, 0, 0, 0, 0): an MFMA
+    # over such fragments adds 16 to each accumulator; the copies of mode 2
+    # bring all-ones rows (an MFMA then adds 32) from the second K tile on
+    rows = 4096
+    src = torch.ones(rows * 64, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((blocks,), -1.0, dtype=torch.float32, device="cuda")
+    B.moe_probe_gemm_slice(mode, src, rows, iters, out, blocks)
+    torch.cuda.synchronize()
+    want = 32.0 * iters if mode < 2 else 32.0 + 64.0 * (iters - 1)
+    assert (out.cpu().numpy() == want).all()
 
 
 @pytest.mark.parametrize("iters,blocks", [(1, 1), (1000, 64), (1 << 19, 2)])
