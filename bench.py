@@ -522,14 +522,16 @@ def main():
 
     # the expert GEMM's K-slice mix alone (one 8-wave block per CU): its
     # MFMAs, + the fragment reads from LDS, + the direct-to-LDS copies of
-    # the next K tile from an L2-resident 2 MiB source
+    # the next K tile from an L2-resident 2 MiB source (issued at the K
+    # tile's start, or between the MFMA rows as in the GEMM)
     sl_iters, sl_blocks, sl_rows = 2000, 256, 16384
     sl_src = torch.ones(sl_rows * 64, dtype=torch.bfloat16, device=dev)
     sl_out = torch.empty(sl_blocks, dtype=torch.float32, device=dev)
     sl_flop = 2.0 * 16 * 16 * 32 * 64 * 8 * sl_iters * sl_blocks
     slice_tflops = {name: sl_flop / (best_ms(lambda m=m: B.moe_probe_gemm_slice(
         m, sl_src, sl_rows, sl_iters, sl_out, sl_blocks, stream)) * 1e-3) / 1e12
-        for m, name in ((0, "mfma"), (1, "lds_reads"), (2, "lds_reads_copies"))}
+        for m, name in ((0, "mfma"), (1, "lds_reads"), (2, "lds_reads_copies_at_start"),
+                        (3, "lds_reads_copies"))}
     del sl_src, sl_out
 
     work = algorithmic_work(cfg, counts)

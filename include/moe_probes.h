@@ -87,11 +87,14 @@ int32_t moe_probe_mfma_loop(int64_t iters, float* out, int blocks, moe_stream st
  *   mode 1: + every fragment read from LDS at every 32-wide K step;
  *   mode 2: + the next K tile's 64 KB copied into LDS with direct-to-LDS
  *           loads from src (src_rows rows of 128 bytes, re-read by every
- *           block: keep it a few MB, so that it stays in L2).
+ *           block: keep it a few MB, so that it stays in L2), all issued at
+ *           the K tile's start;
+ *   mode 3: the same copies issued one after every second row of MFMAs,
+ *           the expert GEMM's own order.
  * 2*16*16*32 * 64 * 8 * iters * blocks FLOP.
  *
- * src: device, src_rows * 128 bytes, 16-byte aligned, src_rows >= 512 (mode
- *   2 only; ignored otherwise).  out: device, `blocks` floats, written.
+ * src: device, src_rows * 128 bytes, 16-byte aligned, src_rows >= 512 (modes
+ *   2 and 3 only; ignored otherwise).  out: device, `blocks` floats, written.
  *   iters in [1, 2^20], blocks in [1, 65536].
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE; nothing is written on error.
  *   Asynchronous on `stream`; allocates nothing.

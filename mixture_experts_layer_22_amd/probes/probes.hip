@@ -147,7 +147,9 @@ __global__ __launch_bounds__(256) void k_row_gather(const f32x4* __restrict__ ta
 // ds_read_b128 per wave per step); MODE 2: + the next K tile's 64 KB copied
 // into the other of two LDS buffers with direct-to-LDS loads (8 per thread
 // per K tile) from `src`, src_rows rows of 128 bytes that every block
-// re-reads (a few MB: they stay in L2).  64 MFMAs per wave per K tile.
+// re-reads (a few MB: they stay in L2), all issued at the K tile's start;
+// MODE 3: the same copies issued one after every second MFMA row, the
+// order of the GEMM's own loop.  64 MFMAs per wave per K tile.
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void k_gemm_slice(const uint16_t* __restrict__ src,
                                                        int src_rows, int iters,
@@ -176,30 +178,33 @@ __global__ __launch_bounds__(512, 1) void k_gemm_slice(const uint16_t* __restric
 #pragma unroll
     for (int fn = 0; fn < 4; fn++) bfr[fn] = frag(buf, 256 + wn * 64 + fn * 16 + frow, ks);
   };
+  // copy i (0..7) of the next K tile: wave w fills rows 64w + 8i .. + 7 of
+  // the other buffer
+  auto copy = [&](int it, int cur, int i) {
+    const int r = wave * 64 + 8 * i;
+    const int64_t sr = ((int64_t)(it + 1) * ROWS + r + (lane >> 3)) % src_rows;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + sr * BK + (lane & 7) * 8),
+                                     (lds_void_t*)&lds[cur ^ 1][r * BK], 16, 0, 0);
+  };
   if (MODE == 0) read_frags(0, 0);
   for (int it = 0; it < iters; it++) {
     const int cur = it & 1;
-    if (MODE == 2) {
-      // wave w fills rows 64w .. 64w + 63 of the other buffer, 8 rows per copy
+    if (MODE == 2)
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int r = wave * 64 + 8 * i;
-        const int64_t sr = ((int64_t)(it + 1) * ROWS + r + (lane >> 3)) % src_rows;
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + sr * BK + (lane & 7) * 8),
-                                         (lds_void_t*)&lds[cur ^ 1][r * BK], 16, 0, 0);
-      }
-    }
+      for (int i = 0; i < 8; i++) copy(it, cur, i);
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
       if (MODE >= 1) read_frags(cur, ks);
 #pragma unroll
-      for (int fm = 0; fm < 8; fm++)
+      for (int fm = 0; fm < 8; fm++) {
 #pragma unroll
         for (int fn = 0; fn < 4; fn++)
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], afr[fm], acc[fm][fn],
                                                                 0, 0, 0);
+        if (MODE == 3 && (fm & 1) == 0) copy(it, cur, ks * 4 + fm / 2);
+      }
     }
-    if (MODE == 2) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+    if (MODE >= 2) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
     __syncthreads();
   }
   float s = 0.f;
@@ -284,9 +289,9 @@ extern "C" int32_t moe_probe_mfma_loop(int64_t iters, float* out, int blocks,
 extern "C" int32_t moe_probe_gemm_slice(int mode, const void* src, int src_rows, int iters,
                                         float* out, int blocks, moe_stream stream) {
   using namespace moe_probes;
-  if (!out || (mode == 2 && !src)) return MOE_ERR_NULL;
-  if (mode < 0 || mode > 2 || iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536 ||
-      (mode == 2 && (src_rows < 512 || (uintptr_t)src % 16 != 0)))
+  if (!out || (mode >= 2 && !src)) return MOE_ERR_NULL;
+  if (mode < 0 || mode > 3 || iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536 ||
+      (mode >= 2 && (src_rows < 512 || (uintptr_t)src % 16 != 0)))
     return MOE_ERR_SHAPE;
   const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
   hipStream_t st = (hipStream_t)stream;
@@ -294,8 +299,10 @@ extern "C" int32_t moe_probe_gemm_slice(int mode, const void* src, int src_rows,
     hipLaunchKernelGGL(k_gemm_slice<0>, dim3((unsigned)blocks), dim3(512), 0, st, s16, src_rows, iters, out);
   else if (mode == 1)
     hipLaunchKernelGGL(k_gemm_slice<1>, dim3((unsigned)blocks), dim3(512), 0, st, s16, src_rows, iters, out);
-  else
+  else if (mode == 2)
     hipLaunchKernelGGL(k_gemm_slice<2>, dim3((unsigned)blocks), dim3(512), 0, st, s16, src_rows, iters, out);
+  else
+    hipLaunchKernelGGL(k_gemm_slice<3>, dim3((unsigned)blocks), dim3(512), 0, st, s16, src_rows, iters, out);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -290,7 +290,8 @@ def test_probes_reject_on_host(prb):
     sl = prb.moe_probe_gemm_slice
     assert sl(0, None, 0, 10, None, 4, None) == B.MOE_ERR_NULL
     assert sl(2, None, 4096, 10, P, 4, None) == B.MOE_ERR_NULL     # copies need a source
-    assert sl(3, P, 4096, 10, P, 4, None) == B.MOE_ERR_SHAPE       # no such mode
+    assert sl(4, P, 4096, 10, P, 4, None) == B.MOE_ERR_SHAPE       # no such mode
+    assert sl(3, None, 4096, 10, P, 4, None) == B.MOE_ERR_NULL
     assert sl(2, P, 256, 10, P, 4, None) == B.MOE_ERR_SHAPE        # fewer rows than one K tile
     assert sl(2, P + 4, 4096, 10, P, 4, None) == B.MOE_ERR_SHAPE   # misaligned
     assert sl(1, None, 0, 0, P, 4, None) == B.MOE_ERR_SHAPE

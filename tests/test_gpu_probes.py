@@ -51,11 +51,11 @@ def test_stream_read_blocks_reads_every_element(n, blocks):
 
 
 @pytest.mark.parametrize("mode,iters,blocks", [(0, 1, 1), (0, 300, 7), (1, 300, 7), (2, 1, 3),
-                                               (2, 300, 256)])
+                                               (2, 300, 256), (3, 1, 3), (3, 300, 256)])
 def test_gemm_slice_runs_every_mfma(mode, iters, blocks):
     # every 16-byte LDS chunk starts as bf16 (1, 1, 1, 1, 0, 0, 0, 0): an MFMA
-    # over such fragments adds 16 to each accumulator; the copies of mode 2
-    # bring all-ones rows (an MFMA then adds 32) from the second K tile on
+    # over such fragments adds 16 to each accumulator; the copies of modes 2
+    # and 3 bring all-ones rows (an MFMA then adds 32) from the second K tile on
     rows = 4096
     src = torch.ones(rows * 64, dtype=torch.bfloat16, device="cuda")
     out = torch.full((blocks,), -1.0, dtype=torch.float32, device="cuda")
