@@ -89,8 +89,8 @@ int32_t moe_probe_mfma_loop(int64_t iters, float* out, int blocks, moe_stream st
  *           loads from src (src_rows rows of 128 bytes, re-read by every
  *           block: keep it a few MB, so that it stays in L2), all issued at
  *           the K tile's start;
- *   mode 3: the same copies issued one after every second row of MFMAs,
- *           the expert GEMM's own order.
+ *   mode 3: the same copies issued one after each row of MFMAs of the K
+ *           tile's first 32-wide step, the expert GEMM's own order.
  * 2*16*16*32 * 64 * 8 * iters * blocks FLOP.
  *
  * src: device, src_rows * 128 bytes, 16-byte aligned, src_rows >= 512 (modes

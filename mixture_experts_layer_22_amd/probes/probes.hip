@@ -148,8 +148,10 @@ __global__ __launch_bounds__(256) void k_row_gather(const f32x4* __restrict__ ta
 // into the other of two LDS buffers with direct-to-LDS loads (8 per thread
 // per K tile) from `src`, src_rows rows of 128 bytes that every block
 // re-reads (a few MB: they stay in L2), all issued at the K tile's start;
-// MODE 3: the same copies issued one after every second MFMA row, the
-// order of the GEMM's own loop.  64 MFMAs per wave per K tile.
+// MODE 3: the same copies issued one after each MFMA row of the K tile's
+// first 32-wide step, the order of the GEMM's own loop (which issues its
+// copies over the rows of the step that follows its barrier).  64 MFMAs per
+// wave per K tile.
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void k_gemm_slice(const uint16_t* __restrict__ src,
                                                        int src_rows, int iters,
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_slice(const uint16_t* __restric
         for (int fn = 0; fn < 4; fn++)
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], afr[fm], acc[fm][fn],
                                                                 0, 0, 0);
-        if (MODE == 3 && (fm & 1) == 0) copy(it, cur, ks * 4 + fm / 2);
+        if (MODE == 3 && ks == 0) copy(it, cur, fm);
       }
     }
     if (MODE >= 2) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
