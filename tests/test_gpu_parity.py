@@ -219,6 +219,34 @@ def test_ragged_T(T):
     _forward_vs_oracle(cfg, I.make_inputs(cfg))
 
 
+@pytest.mark.parametrize("variant", ["shared", "zero_copy"])
+def test_combine_kernels_agree(variant):
+    """Batches of at most 256 tokens combine with one wave per token and
+    512-column slice, larger ones with one wave per token: the same additions
+    in the same order, so the first 256 tokens of a 300-token batch come out
+    bit for bit the same from both (same routing, same expert outputs)."""
+    if variant == "shared":
+        cfg = I.small_variant("deepseek16b").replace(T=300)
+    else:
+        cfg = I.small_variant("moepp").replace(
+            T=300, zc_kinds=[I.ZC_ZERO, I.ZC_COPY, I.ZC_ZERO, I.ZC_COPY])
+    say("combine kernels agree", variant)
+    inp = I.make_inputs(cfg)
+    layer = make_layer(cfg, inp)
+    x = x_dev(inp)
+    idx, gate = layer.route(x)
+    counts, offsets, perm, inv = layer.dispatch(idx)
+    y, sy = layer.expert_ffn(x, idx, perm, offsets)
+    whole = layer.combine(x, idx, gate, inv, y, sy)
+    part = layer.combine(x[:256].contiguous(), idx[:256].contiguous(), gate[:256].contiguous(),
+                         inv[:256 * cfg.k].contiguous(), y, sy)
+    torch.cuda.synchronize()
+    assert torch.equal(whole[:256], part)
+    idx_np = idx.cpu().numpy()
+    ref, _, _ = O.forward(cfg, inp, idx_np, gate.cpu().numpy().astype(np.float64))
+    assert C.max_rel_l2(np_of(whole), ref) <= C.out_tol(cfg)
+
+
 def test_T_zero():
     cfg = I.small_variant("moepp")
     inp = I.make_inputs(cfg)
