@@ -420,6 +420,35 @@ def test_random_layers(cfg):
     _forward_vs_oracle(cfg, I.make_inputs(cfg))
 
 
+def _random_wide_layers(n=4, seed=2026):
+    """Seeded random softmax-router layers at model widths (d up to 2048, f
+    up to 1024: K loops of up to 32 tiles in both GEMMs), mostly on the
+    256-row tile path, with shared experts and zero-computation experts but
+    no constant ones; outputs checked on sampled tokens."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E_ffn = int(rng.integers(2, 9))
+        n_zc = int(rng.integers(0, 3))
+        k = int(rng.integers(1, min(E_ffn + n_zc, 4) + 1))
+        n_shared = int(rng.integers(0, 3))
+        out.append(I.LayerConfig(
+            name=f"random_wide{i}", T=int(rng.integers(300, 1300)),
+            d=(2048, 1024, 2048, 512)[i % 4], E=E_ffn + n_zc, E_ffn=E_ffn, k=k,
+            f=int(rng.choice([256, 512, 1024])), dtype=I.DT_BF16,
+            n_shared=n_shared, f_shared=int(rng.choice([256, 512])) if n_shared else 0,
+            renorm=bool(rng.random() < 0.5), zipf_s=1.1 if rng.random() < 0.5 else None,
+            zc_kinds=[int(z) for z in rng.integers(0, 2, size=n_zc)], seed=300 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_wide_layers(), ids=lambda c: c.name)
+def test_random_wide_layers(cfg):
+    say("random wide layer", cfg)
+    tok = np.unique(np.r_[0, np.random.default_rng(3).choice(cfg.T, 64), cfg.T - 1])
+    _forward_vs_oracle(cfg, I.make_inputs(cfg), tokens=tok)
+
+
 def _random_pk_layers(n=8, seed=2025):
     """Seeded random product-key layers of atomic experts: grids up to
     96 x 96, row / column top-k up to 32 (k up to 64), both dtypes, with and
