@@ -491,8 +491,9 @@ def main():
         return best
 
     log("[bench] ceilings")
-    # two read patterns over 2 GiB: one window moving over the buffer
-    # (grid-stride), and every block streaming its own contiguous 1 MiB
+    # read patterns over 2 GiB: one window moving over the buffer
+    # (grid-stride), and every block streaming its own contiguous 1 MiB, with
+    # plain and with non-temporal loads
     n_rd, rd_blocks = (2 << 30) // 4, 8192
     rd_buf = torch.ones(n_rd, dtype=torch.float32, device=dev)
     rd_sums = torch.empty(rd_blocks, dtype=torch.float32, device=dev)
@@ -500,8 +501,10 @@ def main():
         rd_buf, n_rd, rd_sums, rd_blocks, stream)) * 1e-3) / 1e9
     n_bl = n_rd * 4 // (1 << 20)
     read_blocks_gbs = n_rd * 4 / (best_ms(lambda: B.moe_probe_stream_read_blocks(
-        rd_buf, n_rd, rd_sums, n_bl, stream)) * 1e-3) / 1e9
-    read_gbs = max(read_grid_gbs, read_blocks_gbs)
+        rd_buf, n_rd, rd_sums, n_bl, False, stream)) * 1e-3) / 1e9
+    read_nt_gbs = n_rd * 4 / (best_ms(lambda: B.moe_probe_stream_read_blocks(
+        rd_buf, n_rd, rd_sums, n_bl, True, stream)) * 1e-3) / 1e9
+    read_gbs = max(read_grid_gbs, read_blocks_gbs, read_nt_gbs)
     del rd_buf, rd_sums
     gather_gbs = None
     if cfg.router == I.ROUTER_PRODUCT_KEY:
@@ -540,7 +543,8 @@ def main():
     # beside the datasheet peaks: what this GPU streams and multiplies when
     # nothing else runs
     ceiling = {"hbm_read_gbs": read_gbs, "hbm_read_grid_stride_gbs": read_grid_gbs,
-               "hbm_read_blocks_gbs": read_blocks_gbs, "mfma_bf16_tflops": mfma_tflops,
+               "hbm_read_blocks_gbs": read_blocks_gbs, "hbm_read_nontemporal_gbs": read_nt_gbs,
+               "mfma_bf16_tflops": mfma_tflops,
                "gemm_slice_tflops": slice_tflops,
                "frac_of_measured": roof["achieved"] / (read_gbs if roof["unit"] == "GB/s"
                                                        else mfma_tflops)}

@@ -27,7 +27,9 @@ int32_t moe_probe_stream_read(const float* buf, int64_t n, float* block_sums, in
 /* Block-contiguous streaming read: block b sums floats
  * [b n/blocks, (b+1) n/blocks) with 16-byte loads, 32 KB per step (512
  * threads, four loads each).  Concurrent reads fall in `blocks` separate
- * regions instead of one window moving over the buffer.
+ * regions instead of one window moving over the buffer.  nontemporal != 0:
+ * the loads carry the non-temporal hint (data read once, not kept in the
+ * caches).
  *
  * buf: device, n floats, 16-byte aligned; n a multiple of 8192 * blocks.
  * block_sums: device, `blocks` floats, written.  blocks in [1, 65536].
@@ -35,7 +37,7 @@ int32_t moe_probe_stream_read(const float* buf, int64_t n, float* block_sums, in
  *   Asynchronous on `stream`; allocates nothing.
  */
 int32_t moe_probe_stream_read_blocks(const float* buf, int64_t n, float* block_sums, int blocks,
-                                     moe_stream stream);
+                                     int nontemporal, moe_stream stream);
 
 /* The same read through direct-to-LDS loads (global_load_lds, the expert
  * GEMM's load kind): block b streams floats [b n/blocks, (b+1) n/blocks),

@@ -299,7 +299,8 @@ def load_probes(path: str = PRB_PATH) -> ctypes.CDLL:
     lib.moe_probe_stream_read.restype = ctypes.c_int32
     lib.moe_probe_stream_read.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
     lib.moe_probe_stream_read_blocks.restype = ctypes.c_int32
-    lib.moe_probe_stream_read_blocks.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
+    lib.moe_probe_stream_read_blocks.argtypes = [P, ctypes.c_int64, P, ctypes.c_int,
+                                                 ctypes.c_int, P]
     lib.moe_probe_stream_read_lds.restype = ctypes.c_int32
     lib.moe_probe_stream_read_lds.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
     lib.moe_probe_row_gather.restype = ctypes.c_int32
@@ -319,9 +320,10 @@ def moe_probe_stream_read(buf, n, block_sums, blocks, stream=None):
                                                _stream(stream)), "moe_probe_stream_read")
 
 
-def moe_probe_stream_read_blocks(buf, n, block_sums, blocks, stream=None):
+def moe_probe_stream_read_blocks(buf, n, block_sums, blocks, nontemporal=False, stream=None):
     _check(load_probes().moe_probe_stream_read_blocks(_ptr(buf), int(n), _ptr(block_sums),
-                                                      int(blocks), _stream(stream)),
+                                                      int(blocks), int(bool(nontemporal)),
+                                                      _stream(stream)),
            "moe_probe_stream_read_blocks")
 
 

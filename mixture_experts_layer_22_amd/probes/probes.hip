@@ -42,17 +42,23 @@ __global__ __launch_bounds__(256) void k_stream_read(const f32x4* __restrict__ b
 // Block-contiguous streaming read: block b reads its own contiguous share
 // [b n/blocks, (b+1) n/blocks) in 32 KB steps (512 threads, four 16-byte
 // loads each, issued together), so that concurrent reads fall in `blocks`
-// separate regions rather than in one window moving over the buffer.
+// separate regions rather than in one window moving over the buffer.  NT:
+// the loads carry the non-temporal hint.
+template <bool NT>
 __global__ __launch_bounds__(512) void k_stream_read_blocks(const f32x4* __restrict__ buf,
                                                             int64_t per_block,
                                                             float* __restrict__ block_sums) {
   __shared__ float ws[8];
   const f32x4* base = buf + (int64_t)blockIdx.x * per_block;
   const int tid = threadIdx.x;
+  auto ld = [](const f32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+  };
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
   for (int64_t off = 0; off < per_block; off += 2048) {
-    const f32x4 a = base[off + tid], b = base[off + 512 + tid], c = base[off + 1024 + tid],
-                d = base[off + 1536 + tid];
+    const f32x4 a = ld(base + off + tid), b = ld(base + off + 512 + tid),
+                c = ld(base + off + 1024 + tid), d = ld(base + off + 1536 + tid);
     s0 += (a[0] + a[1]) + (a[2] + a[3]);
     s1 += (b[0] + b[1]) + (b[2] + b[3]);
     s2 += (c[0] + c[1]) + (c[2] + c[3]);
@@ -254,15 +260,19 @@ extern "C" int32_t moe_probe_stream_read(const float* buf, int64_t n, float* blo
 }
 
 extern "C" int32_t moe_probe_stream_read_blocks(const float* buf, int64_t n, float* block_sums,
-                                                int blocks, moe_stream stream) {
+                                                int blocks, int nontemporal, moe_stream stream) {
   using namespace moe_probes;
   if (!buf || !block_sums) return MOE_ERR_NULL;
   if (n < 0 || blocks < 1 || blocks > 65536 || (uintptr_t)buf % 16 != 0 ||
       n % ((int64_t)blocks * 8192) != 0)
     return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(k_stream_read_blocks, dim3((unsigned)blocks), dim3(512), 0,
-                     (hipStream_t)stream, reinterpret_cast<const f32x4*>(buf), n / 4 / blocks,
-                     block_sums);
+  const f32x4* b4 = reinterpret_cast<const f32x4*>(buf);
+  if (nontemporal)
+    hipLaunchKernelGGL(k_stream_read_blocks<true>, dim3((unsigned)blocks), dim3(512), 0,
+                       (hipStream_t)stream, b4, n / 4 / blocks, block_sums);
+  else
+    hipLaunchKernelGGL(k_stream_read_blocks<false>, dim3((unsigned)blocks), dim3(512), 0,
+                       (hipStream_t)stream, b4, n / 4 / blocks, block_sums);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

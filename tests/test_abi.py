@@ -281,12 +281,12 @@ def test_probes_reject_on_host(prb):
     assert rl(P + 4, 4096, P, 1, None) == B.MOE_ERR_SHAPE    # misaligned
     assert rl(P, 4096, P, 0, None) == B.MOE_ERR_SHAPE
     rb = prb.moe_probe_stream_read_blocks
-    assert rb(None, 8192, P, 1, None) == B.MOE_ERR_NULL
-    assert rb(P, 8192, None, 1, None) == B.MOE_ERR_NULL
-    assert rb(P, 8192 + 4, P, 1, None) == B.MOE_ERR_SHAPE    # not whole 32 KB steps per block
-    assert rb(P, 8192, P, 2, None) == B.MOE_ERR_SHAPE        # 4096 floats per block
-    assert rb(P + 4, 8192, P, 1, None) == B.MOE_ERR_SHAPE    # misaligned
-    assert rb(P, 8192, P, 0, None) == B.MOE_ERR_SHAPE
+    assert rb(None, 8192, P, 1, 0, None) == B.MOE_ERR_NULL
+    assert rb(P, 8192, None, 1, 1, None) == B.MOE_ERR_NULL
+    assert rb(P, 8192 + 4, P, 1, 0, None) == B.MOE_ERR_SHAPE    # not whole 32 KB steps per block
+    assert rb(P, 8192, P, 2, 1, None) == B.MOE_ERR_SHAPE        # 4096 floats per block
+    assert rb(P + 4, 8192, P, 1, 0, None) == B.MOE_ERR_SHAPE    # misaligned
+    assert rb(P, 8192, P, 0, 0, None) == B.MOE_ERR_SHAPE
     sl = prb.moe_probe_gemm_slice
     assert sl(0, None, 0, 10, None, 4, None) == B.MOE_ERR_NULL
     assert sl(2, None, 4096, 10, P, 4, None) == B.MOE_ERR_NULL     # copies need a source

@@ -37,12 +37,13 @@ def test_stream_read_lds_reads_every_element(n, blocks):
     assert np.array_equal(sums.cpu().numpy().astype(np.float64), np.array(want, np.float64))
 
 
+@pytest.mark.parametrize("nt", [False, True])
 @pytest.mark.parametrize("n,blocks", [(8192, 1), (1 << 20, 8), (300 * 8192, 300)])
-def test_stream_read_blocks_reads_every_element(n, blocks):
+def test_stream_read_blocks_reads_every_element(n, blocks, nt):
     buf = torch.ones(n, dtype=torch.float32, device="cuda")
     buf[::1000] = 3.0
     sums = torch.full((blocks,), -1.0, dtype=torch.float32, device="cuda")
-    B.moe_probe_stream_read_blocks(buf, n, sums, blocks)
+    B.moe_probe_stream_read_blocks(buf, n, sums, blocks, nt)
     torch.cuda.synchronize()
     per = n // blocks
     want = [per + 2 * len(range((b * per + 999) // 1000 * 1000, (b + 1) * per, 1000))
